@@ -17,9 +17,9 @@
  * method reaches this result up to the rounding of its staged operands).
  * The loss scale `gscale` cancels exactly in the method and does not appear.
  *
- * Determinism: tokens are cut into fixed blocks of ORACLE_TBLK; each block
- * sums its tokens in order, and block partials are added in block order, so
- * results do not depend on the thread count.
+ * Determinism: every sum runs in a fixed order (over k, i, j inside a
+ * token; over tokens in order for the column sums), so results do not
+ * depend on the thread count.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -27,8 +27,6 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
-
-#define ORACLE_TBLK 64
 
 int oracle_threads(void) {
 #ifdef _OPENMP
@@ -128,82 +126,74 @@ int oracle_blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const 
     return bad ? -1 : 0;
 }
 
+/* out[col] += sum over t = 0..M-1 (in order) of P[t][col] Q[t][col]
+ * (`colsum_prod` shader). Columns are split over threads in fixed ranges of
+ * 64; each thread walks the tokens in order over its range. */
+static void colsum_prod(int64_t M, int64_t n, const double *P, const double *Q, double *out) {
+    int64_t nch = (n + 63) / 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        int64_t c0 = ch * 64, c1 = c0 + 64 < n ? c0 + 64 : n;
+        double acc[64];
+        for (int64_t c = c0; c < c1; ++c) acc[c - c0] = 0.0;
+        for (int64_t t = 0; t < M; ++t)
+            for (int64_t c = c0; c < c1; ++c) acc[c - c0] += P[t * n + c] * Q[t * n + c];
+        for (int64_t c = c0; c < c1; ++c) out[c] += acc[c - c0];
+    }
+}
+
 /* Backward (`blr_backward`; doc block, backward lines), recomputing a and c
  * from x (the method keeps them as a tape of the last forward on the same x):
  *   dh[i] += sum_t dy[t][i] c[t][i]
- *   db[k]  = sum_i dy[i] h[i] S_U[i][k]                 (per token)
+ *   db[t][k] = sum_i dy[t][i] h[i] S_U[i][k]
  *   dl[k] += sum_t a[t][k] db[t][k]
- *   dx'[j] = sum_k db[k] l[k] S_V[j][k]                 (per token)
+ *   dx'[t][j] = sum_k db[t][k] l[k] S_V[j][k]
  *   dg[j] += sum_t x[t][j] dx'[t][j]
  *   dx[t][j] = (accumulate_dx ? dx[t][j] : 0) + g[j] dx'[t][j]
- * dh, dl, dg always accumulate (the caller zeroes them). Returns 0, or -1
+ * dh, dl, dg always accumulate (the caller zeroes them). The per-token
+ * arrays are formed first (in parallel over tokens), then each column sum
+ * runs over the tokens in order (in parallel over columns). Returns 0, or -1
  * when memory runs out. */
 int oracle_blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const double *x, const double *dy,
                         const uint32_t *bits_u, const uint32_t *bits_v, const double *h, const double *l,
                         const double *g, double *dh, double *dl, double *dg, double *dx, int accumulate_dx) {
-    int64_t nblk = (M + ORACLE_TBLK - 1) / ORACLE_TBLK;
     double *SU = decode_alloc(bits_u, d_out, r);
     double *SV = decode_alloc(bits_v, d_in, r);
-    double *ph = (double *)calloc((size_t)(nblk * d_out), sizeof(double));
-    double *pl = (double *)calloc((size_t)(nblk * r), sizeof(double));
-    double *pg = (double *)calloc((size_t)(nblk * d_in), sizeof(double));
-    int bad = (SU == NULL || SV == NULL || ph == NULL || pl == NULL || pg == NULL);
+    double *A = (double *)malloc((size_t)(M * r) * sizeof(double));
+    double *C = (double *)malloc((size_t)(M * d_out) * sizeof(double));
+    double *DB = (double *)malloc((size_t)(M * r) * sizeof(double));
+    double *DXP = (double *)malloc((size_t)(M * d_in) * sizeof(double));
+    int bad = (SU == NULL || SV == NULL || A == NULL || C == NULL || DB == NULL || DXP == NULL);
     if (!bad) {
-#pragma omp parallel
-        {
-            double *a = (double *)malloc((size_t)r * sizeof(double));
-            double *c = (double *)malloc((size_t)d_out * sizeof(double));
-            double *db = (double *)malloc((size_t)r * sizeof(double));
-            double *dxp = (double *)malloc((size_t)d_in * sizeof(double));
-            if (a == NULL || c == NULL || db == NULL || dxp == NULL) {
-#pragma omp atomic write
-                bad = 1;
-            } else {
-#pragma omp for schedule(static)
-                for (int64_t b = 0; b < nblk; ++b) {
-                    int64_t t1 = (b + 1) * ORACLE_TBLK < M ? (b + 1) * ORACLE_TBLK : M;
-                    for (int64_t t = b * ORACLE_TBLK; t < t1; ++t) {
-                        const double *xt = x + t * d_in;
-                        const double *dyt = dy + t * d_out;
-                        token_forward(d_in, d_out, r, xt, SU, SV, l, g, a, c);
-                        for (int64_t i = 0; i < d_out; ++i) ph[b * d_out + i] += dyt[i] * c[i];
-                        for (int64_t k = 0; k < r; ++k) db[k] = 0.0;
-                        for (int64_t i = 0; i < d_out; ++i) {
-                            double dyh = dyt[i] * h[i];
-                            const double *su = SU + i * r;
-                            for (int64_t k = 0; k < r; ++k) db[k] += dyh * su[k];
-                        }
-                        for (int64_t k = 0; k < r; ++k) pl[b * r + k] += a[k] * db[k];
-                        for (int64_t j = 0; j < d_in; ++j) {
-                            const double *sv = SV + j * r;
-                            double s = 0.0;
-                            for (int64_t k = 0; k < r; ++k) s += db[k] * l[k] * sv[k];
-                            dxp[j] = s;
-                        }
-                        for (int64_t j = 0; j < d_in; ++j) {
-                            pg[b * d_in + j] += xt[j] * dxp[j];
-                            dx[t * d_in + j] = (accumulate_dx ? dx[t * d_in + j] : 0.0) + g[j] * dxp[j];
-                        }
-                    }
-                }
+#pragma omp parallel for schedule(static)
+        for (int64_t t = 0; t < M; ++t) {
+            const double *dyt = dy + t * d_out;
+            double *a = A + t * r, *db = DB + t * r, *dxp = DXP + t * d_in;
+            token_forward(d_in, d_out, r, x + t * d_in, SU, SV, l, g, a, C + t * d_out);
+            for (int64_t k = 0; k < r; ++k) db[k] = 0.0;
+            for (int64_t i = 0; i < d_out; ++i) {
+                double dyh = dyt[i] * h[i];
+                const double *su = SU + i * r;
+                for (int64_t k = 0; k < r; ++k) db[k] += dyh * su[k];
             }
-            free(a);
-            free(c);
-            free(db);
-            free(dxp);
+            for (int64_t j = 0; j < d_in; ++j) {
+                const double *sv = SV + j * r;
+                double s = 0.0;
+                for (int64_t k = 0; k < r; ++k) s += db[k] * l[k] * sv[k];
+                dxp[j] = s;
+            }
+            for (int64_t j = 0; j < d_in; ++j)
+                dx[t * d_in + j] = (accumulate_dx ? dx[t * d_in + j] : 0.0) + g[j] * dxp[j];
         }
-    }
-    if (!bad) {
-        for (int64_t b = 0; b < nblk; ++b) {
-            for (int64_t i = 0; i < d_out; ++i) dh[i] += ph[b * d_out + i];
-            for (int64_t k = 0; k < r; ++k) dl[k] += pl[b * r + k];
-            for (int64_t j = 0; j < d_in; ++j) dg[j] += pg[b * d_in + j];
-        }
+        colsum_prod(M, d_out, dy, C, dh);
+        colsum_prod(M, r, A, DB, dl);
+        colsum_prod(M, d_in, x, DXP, dg);
     }
     free(SU);
     free(SV);
-    free(ph);
-    free(pl);
-    free(pg);
+    free(A);
+    free(C);
+    free(DB);
+    free(DXP);
     return bad ? -1 : 0;
 }
