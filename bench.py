@@ -1,0 +1,224 @@
+"""Benchmark of the `blr` layer's forward + backward on one MI355X.
+
+One step = blr_forward + blr_backward (all steps of the layer) over one
+batch of seeded synthetic input that is already resident in HBM. Default
+workload: the attention-projection layer M=8192 tokens, d_in=d_out=4096,
+r=512. Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+# MI355X published peaks
+PEAK_F16_TFLOPS = 2516.6  # dense f16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0     # HBM3E
+RIDGE = PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
+
+
+def kernel_work(name: str, w: synth.Workload) -> tuple[float, float]:
+    """Algorithmic (bytes, flops) of one launch of a kernel: the bytes each
+    kernel must move between HBM and the chip at minimum (f32 activations,
+    f16 sign planes read once) and the MFMA flops of its contraction."""
+    M, di, do, r = w.M, w.d_in, w.d_out, w.r
+    f32, f16 = 4, 2
+    if name == "gemm_f1_xg_sv":      # read x, write tape a, plane [r][d_in]
+        return M * (di + r) * f32 + r * di * f16 + di * f32, 2.0 * M * r * di
+    if name == "gemm_f2_al_sut":     # read a, write tape c and y, plane [d_out][r]
+        return M * (r + 2 * do) * f32 + do * r * f16 + (r + do) * f32, 2.0 * M * do * r
+    if name == "gemm_b1_dyh_su":     # read dy and a, write db, plane [r][d_out]
+        return M * (do + 2 * r) * f32 + r * do * f16 + do * f32, 2.0 * M * r * do
+    if name == "gemm_b2_dbl_svt":    # read db and x, write dx, plane [d_in][r]
+        return M * (r + 2 * di) * f32 + di * r * f16 + (r + di) * f32, 2.0 * M * di * r
+    if name == "colsum_dy_c":        # read dy and c
+        return 2.0 * M * do * f32, 2.0 * M * do
+    if name == "expand_signs":       # per launch: one bitmap in, one f16 plane out (average of U and V)
+        rows = (di + do) / 2
+        return rows * (r / 8 + r * f16), 0.0
+    return 0.0, 0.0
+
+
+def gen_inputs(w: synth.Workload, dev):
+    import torch
+    d = synth.inputs(w)
+    t = {}
+    for k, v in d.items():
+        if v.dtype == np.uint32:
+            v = v.view(np.int32)
+        t[k] = torch.from_numpy(v).to(dev)
+    return d, t
+
+
+def cpu_baseline(w: synth.Workload, d: dict, target_s: float = 12.0) -> dict:
+    """The f64 oracle, as it stands, on the first tokens of the same inputs:
+    a 1024-token calibration run, then a sample sized to about target_s."""
+    import oracle
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.forward(d["x"][:n], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"], tape=False)
+        oracle.backward(d["x"][:n], d["dy"][:n], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"])
+        return time.perf_counter() - t0
+
+    n = min(w.M, 1024)
+    dt = run(n)
+    if dt < 0.4 * target_s and n < w.M:
+        n = int(min(w.M, max(n, n * target_s / dt)))
+        n = max(64, (n // 64) * 64)
+        dt = run(n)
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"first {n} of {w.M} tokens of the same workload, fwd+bwd in f64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer's data-parallel split and its "
+              "gradient all-reduce are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import binary_rank_linear_amd as blr
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    blr.load()
+    if not blr.device_supported(0):
+        raise SystemExit("cuda:0 is not gfx950")
+    print(f"# workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    d, t = gen_inputs(w, dev)
+    M, di, do, r = w.M, w.d_in, w.d_out, w.r
+    y = torch.empty((M, do), dtype=torch.float32, device=dev)
+    ta = torch.empty((M, r), dtype=torch.float32, device=dev)
+    tc = torch.empty((M, do), dtype=torch.float32, device=dev)
+    dx = torch.empty((M, di), dtype=torch.float32, device=dev)
+    dh = torch.zeros(do, dtype=torch.float32, device=dev)
+    dl = torch.zeros(r, dtype=torch.float32, device=dev)
+    dg = torch.zeros(di, dtype=torch.float32, device=dev)
+    ws = blr.workspace(M, di, do, r, dev)
+
+    def fwd():
+        blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], y=y, tape_a=ta, tape_c=tc, ws=ws)
+
+    def bwd():
+        blr.blr_backward(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc, w.gscale,
+                         dh=dh, dl=dl, dg=dg, dx=dx, ws=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # forward and backward alone (context)
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    fwd_ms = timed(fwd, args.steps)
+    bwd_ms = timed(bwd, args.steps)
+
+    # per-kernel durations: HIP events the library records around each of its
+    # launches, on the launch stream, over a second timed region of K steps
+    blr.blr_profile_enable(args.steps * 16)
+    blr.blr_profile_reset()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = blr.blr_profile_read()
+    blr.blr_profile_enable(0)
+    kernels = {}
+    for name, (count, tot_ms) in prof.items():
+        avg_us = 1000.0 * tot_ms / count
+        nbytes, flops = kernel_work(name, w)
+        kernels[name] = {"launches_per_step": count / args.steps, "avg_us": round(avg_us, 3),
+                         "gbs": round(nbytes / (avg_us * 1e-6) / 1e9, 1) if nbytes else None,
+                         "tflops": round(flops / (avg_us * 1e-6) / 1e12, 1) if flops else None}
+    dom = max(prof, key=lambda k: prof[k][1])
+    nbytes, flops = kernel_work(dom, w)
+    avg_s = prof[dom][1] / prof[dom][0] / 1000.0
+    if flops and flops / nbytes > RIDGE:
+        roof = {"bound": "mfma", "achieved": round(flops / avg_s / 1e12, 2), "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_us"] = round(avg_s * 1e6, 3)
+
+    tokens_s = M / (ms / 1000.0)
+    tf_metric = w.flops_metric() / (ms / 1000.0) / 1e12
+    tf_mfma = w.flops_mfma() / (ms / 1000.0) / 1e12
+    out = {
+        "metric": "blr fwd+bwd tokens/s and TFLOP/s (% of f16 MFMA peak) at d=4096, r=512",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "d_in": di, "d_out": do, "r": r, "gscale": w.gscale,
+                   "accumulate": "f32", "paths": 1},
+        "tflops_metric": round(tf_metric, 2),
+        "pct_f16_peak_metric": round(100 * tf_metric / PEAK_F16_TFLOPS, 2),
+        "tflops_mfma": round(tf_mfma, 2),
+        "pct_f16_peak_mfma": round(100 * tf_mfma / PEAK_F16_TFLOPS, 2),
+        "fwd_ms": round(fwd_ms, 5),
+        "bwd_ms": round(bwd_ms, 5),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("# oracle CPU baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, d)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

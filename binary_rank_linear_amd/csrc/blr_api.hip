@@ -1,0 +1,345 @@
+// C ABI of the `blr` layer (include/blr.h): argument validation, workspace
+// layout and launch order on the caller's stream. The order of the steps is
+// the one of `blr_forward` / `blr_backward` on the cortiq-engine page
+// "src/gpu_wgpu/train_mm.rs"; their staging and scaling passes live inside
+// the contraction kernels.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/blr.h"
+#include "blr_internal.h"
+
+namespace blr {
+
+// ------------------------------------------------------------ profiling --
+namespace {
+struct ProfState {
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // pairs
+    std::vector<int> ids;        // kernel id per recorded pair
+    size_t used = 0;
+    int pending_id = -1;
+    int64_t counts[K_COUNT] = {};
+    double total_ms[K_COUNT] = {};
+};
+ProfState g_prof;
+std::mutex g_prof_mu;
+
+void prof_release() {
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.ids.clear();
+    g_prof.used = 0;
+    g_prof.on = false;
+}
+}  // namespace
+
+void prof_begin(int id, hipStream_t s) {
+    if (!g_prof.on) return;
+    g_prof.pending_id = -1;
+    if (2 * (g_prof.used + 1) > g_prof.ev.size()) return;  // pool full: launch goes untimed
+    (void)hipEventRecord(g_prof.ev[2 * g_prof.used], s);
+    g_prof.pending_id = id;
+}
+
+void prof_end(hipStream_t s) {
+    if (!g_prof.on || g_prof.pending_id < 0) return;
+    (void)hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
+    g_prof.ids.push_back(g_prof.pending_id);
+    g_prof.used += 1;
+    g_prof.pending_id = -1;
+}
+
+// ------------------------------------------------------------ workspace --
+namespace {
+constexpr size_t ALIGN = 256;
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+    size_t plane_u, plane_v;  // f16 planes (one orientation each per call)
+    size_t db;                // f32 [M][r]
+    size_t part_h, part_l, part_g;
+    size_t total;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+    Layout L;
+    size_t off = 0;
+    L.plane_u = off;
+    off += up((size_t)(d_out * r) * 2);
+    L.plane_v = off;
+    off += up((size_t)(d_in * r) * 2);
+    L.db = off;
+    off += up((size_t)(M * r) * 4);
+    L.part_h = off;
+    off += up((size_t)(ceil_div(M, COLSUM_ROWS) * d_out) * 4);
+    L.part_l = off;
+    off += up((size_t)(ceil_div(M, GEMM_BM) * r) * 4);
+    L.part_g = off;
+    off += up((size_t)(ceil_div(M, GEMM_BM) * d_in) * 4);
+    L.total = off;
+    return L;
+}
+
+// Sizes the kernels accept: d_in, d_out, r multiples of 128 (the page's GEMM
+// contract), M >= 1, and everything small enough for 32-bit grid and column
+// indices.
+bool shape_ok(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+    if (M < 1 || d_in < 128 || d_out < 128 || r < 128) return false;
+    if (d_in % 128 || d_out % 128 || r % 128) return false;
+    const int64_t LIM = (int64_t)1 << 24;  // columns and ranks
+    if (d_in > LIM || d_out > LIM || r > LIM) return false;
+    if (ceil_div(M, GEMM_BM) > 65535 || ceil_div(M, COLSUM_ROWS) > 65535) return false;
+    return true;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool pow2_scale_ok(float s) {
+    if (!(s > 0.0f) || !isfinite(s)) return false;
+    int e;
+    return frexpf(s, &e) == 0.5f;
+}
+
+int g_supported[64];  // 0 unknown, 1 yes, -1 no
+std::mutex g_dev_mu;
+
+int current_device_ok() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BLR_ERR_HIP;
+    if (dev < 0 || dev >= 64) return blr_device_supported(dev) ? BLR_OK : BLR_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_supported[dev] == 0) g_supported[dev] = blr_device_supported(dev) ? 1 : -1;
+    return g_supported[dev] == 1 ? BLR_OK : BLR_ERR_DEVICE;
+}
+
+#define BLR_TRY(expr)                                   \
+    do {                                                \
+        if ((expr) != hipSuccess) return BLR_ERR_HIP;   \
+    } while (0)
+}  // namespace
+
+}  // namespace blr
+
+using namespace blr;
+
+extern "C" {
+
+const char *blr_status_string(int status) {
+    switch (status) {
+        case BLR_OK: return "ok";
+        case BLR_ERR_NULL: return "a required pointer is NULL";
+        case BLR_ERR_SHAPE: return "invalid shape (d_in, d_out, r must be multiples of 128; M >= 1)";
+        case BLR_ERR_SCALE: return "gscale must be a positive finite power of two";
+        case BLR_ERR_WORKSPACE: return "workspace missing or smaller than blr_workspace_bytes()";
+        case BLR_ERR_DEVICE: return "the current device is not gfx950";
+        case BLR_ERR_HIP: return "HIP runtime error";
+        case BLR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+int blr_device_supported(int hip_device) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, hip_device) != hipSuccess) return 0;
+    return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+size_t blr_workspace_bytes(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+    if (!shape_ok(M, d_in, d_out, r)) return 0;
+    return layout(M, d_in, d_out, r).total;
+}
+
+int blr_expand_signs(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *plane, uint16_t *plane_t,
+                     void *stream) {
+    if (bits == nullptr || (plane == nullptr && plane_t == nullptr)) return BLR_ERR_NULL;
+    if (rows < 1 || r < 1 || (rows + 63) / 64 > 65535 || r > ((int64_t)1 << 30) || rows * r > ((int64_t)1 << 40))
+        return BLR_ERR_SHAPE;
+    if (!aligned4(bits) || (plane && !aligned16(plane)) || (plane_t && !aligned16(plane_t))) return BLR_ERR_ALIGN;
+    int st = current_device_ok();
+    if (st != BLR_OK) return st;
+    return launch_expand(bits, rows, r, plane, plane_t, (hipStream_t)stream) == hipSuccess ? BLR_OK : BLR_ERR_HIP;
+}
+
+int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
+                const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y, int accumulate_y,
+                float *tape_a, float *tape_c, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!x || !bits_u || !bits_v || !h || !l || !g || !y || !tape_a || !tape_c) return BLR_ERR_NULL;
+    if (!shape_ok(M, d_in, d_out, r)) return BLR_ERR_SHAPE;
+    const Layout L = layout(M, d_in, d_out, r);
+    if (workspace == nullptr || workspace_bytes < L.total) return BLR_ERR_WORKSPACE;
+    const void *f16a[] = {x, h, l, g, y, tape_a, tape_c, workspace};
+    for (const void *p : f16a)
+        if (!aligned16(p)) return BLR_ERR_ALIGN;
+    if (!aligned4(bits_u) || !aligned4(bits_v)) return BLR_ERR_ALIGN;
+    int st = current_device_ok();
+    if (st != BLR_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    uint16_t *plt_v = (uint16_t *)(ws + L.plane_v);  // S_V^T [r][d_in]
+    uint16_t *pl_u = (uint16_t *)(ws + L.plane_u);   // S_U   [d_out][r]
+
+    BLR_TRY(launch_expand(bits_v, d_in, r, nullptr, plt_v, s));
+    BLR_TRY(launch_expand(bits_u, d_out, r, pl_u, nullptr, s));
+
+    GemmArgs f1 = {};
+    f1.A = x;
+    f1.lda = d_in;
+    f1.colscale = g;
+    f1.ascale = 1.0f;
+    f1.B = plt_v;
+    f1.M = M;
+    f1.N = (int)r;
+    f1.K = (int)d_in;
+    f1.oscale = 1.0f;
+    f1.out = tape_a;
+    BLR_TRY(launch_gemm(GEMM_F1, f1, s));
+
+    GemmArgs f2 = {};
+    f2.A = tape_a;
+    f2.lda = r;
+    f2.colscale = l;
+    f2.ascale = 1.0f;
+    f2.B = pl_u;
+    f2.M = M;
+    f2.N = (int)d_out;
+    f2.K = (int)r;
+    f2.oscale = 1.0f;
+    f2.out = tape_c;
+    f2.out2 = y;
+    f2.out2col = h;
+    f2.out2acc = accumulate_y ? 1 : 0;
+    BLR_TRY(launch_gemm(GEMM_F2, f2, s));
+    return BLR_OK;
+}
+
+int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
+                 const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                 const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl, float *dg, float *dx,
+                 int accumulate_dx, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!x || !dy || !bits_u || !bits_v || !h || !l || !g || !tape_a || !tape_c || !dh || !dl || !dg || !dx)
+        return BLR_ERR_NULL;
+    if (!shape_ok(M, d_in, d_out, r)) return BLR_ERR_SHAPE;
+    if (!pow2_scale_ok(gscale)) return BLR_ERR_SCALE;
+    const Layout L = layout(M, d_in, d_out, r);
+    if (workspace == nullptr || workspace_bytes < L.total) return BLR_ERR_WORKSPACE;
+    const void *f16a[] = {x, dy, h, l, g, tape_a, tape_c, dh, dl, dg, dx, workspace};
+    for (const void *p : f16a)
+        if (!aligned16(p)) return BLR_ERR_ALIGN;
+    if (!aligned4(bits_u) || !aligned4(bits_v)) return BLR_ERR_ALIGN;
+    int st = current_device_ok();
+    if (st != BLR_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    uint16_t *plt_u = (uint16_t *)(ws + L.plane_u);  // S_U^T [r][d_out]
+    uint16_t *pl_v = (uint16_t *)(ws + L.plane_v);   // S_V   [d_in][r]
+    float *db = (float *)(ws + L.db);
+    float *part_h = (float *)(ws + L.part_h);
+    float *part_l = (float *)(ws + L.part_l);
+    float *part_g = (float *)(ws + L.part_g);
+    const float inv = 1.0f / gscale;  // exact: gscale is a power of two
+    const int64_t mt = (M + GEMM_BM - 1) / GEMM_BM;
+
+    BLR_TRY(launch_expand(bits_u, d_out, r, nullptr, plt_u, s));
+    BLR_TRY(launch_expand(bits_v, d_in, r, pl_v, nullptr, s));
+
+    // dh += sum_t dy.c
+    BLR_TRY(launch_colsum(dy, tape_c, M, (int)d_out, part_h, s));
+    BLR_TRY(launch_finish(part_h, (M + COLSUM_ROWS - 1) / COLSUM_ROWS, (int)d_out, dh, s));
+
+    // db = f16(dy.h.gs) S_U / gs; dl += sum_t a.db
+    GemmArgs b1 = {};
+    b1.A = dy;
+    b1.lda = d_out;
+    b1.colscale = h;
+    b1.ascale = gscale;
+    b1.B = plt_u;
+    b1.M = M;
+    b1.N = (int)r;
+    b1.K = (int)d_out;
+    b1.oscale = inv;
+    b1.out = db;
+    b1.dot_other = tape_a;
+    b1.dot_partial = part_l;
+    BLR_TRY(launch_gemm(GEMM_B1, b1, s));
+    BLR_TRY(launch_finish(part_l, mt, (int)r, dl, s));
+
+    // dx' = f16(db.l.gs) S_V^T / gs; dx (+)= g.dx'; dg += sum_t x.dx'
+    GemmArgs b2 = {};
+    b2.A = db;
+    b2.lda = r;
+    b2.colscale = l;
+    b2.ascale = gscale;
+    b2.B = pl_v;
+    b2.M = M;
+    b2.N = (int)d_in;
+    b2.K = (int)r;
+    b2.oscale = inv;
+    b2.out2 = dx;
+    b2.out2col = g;
+    b2.out2acc = accumulate_dx ? 1 : 0;
+    b2.dot_other = x;
+    b2.dot_partial = part_g;
+    BLR_TRY(launch_gemm(GEMM_B2, b2, s));
+    BLR_TRY(launch_finish(part_g, mt, (int)d_in, dg, s));
+    return BLR_OK;
+}
+
+int blr_profile_enable(int max_launches) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    prof_release();
+    if (max_launches <= 0) return BLR_OK;
+    g_prof.ev.resize(2 * (size_t)max_launches);
+    for (size_t i = 0; i < g_prof.ev.size(); ++i) {
+        if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
+            g_prof.ev.resize(i);
+            prof_release();
+            return BLR_ERR_HIP;
+        }
+    }
+    g_prof.on = true;
+    return BLR_OK;
+}
+
+int blr_profile_read(const char **names, int64_t *counts, double *total_ms, int max) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (size_t q = 0; q < g_prof.used; ++q) {
+        if (hipEventSynchronize(g_prof.ev[2 * q + 1]) != hipSuccess) return BLR_ERR_HIP;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, g_prof.ev[2 * q], g_prof.ev[2 * q + 1]) != hipSuccess) return BLR_ERR_HIP;
+        g_prof.counts[g_prof.ids[q]] += 1;
+        g_prof.total_ms[g_prof.ids[q]] += ms;
+    }
+    g_prof.used = 0;
+    g_prof.ids.clear();
+    int n = 0;
+    for (int id = 0; id < K_COUNT; ++id) {
+        if (g_prof.counts[id] == 0) continue;
+        if (n < max) {
+            if (names) names[n] = kernel_name(id);
+            if (counts) counts[n] = g_prof.counts[id];
+            if (total_ms) total_ms[n] = g_prof.total_ms[id];
+        }
+        ++n;
+    }
+    return n;
+}
+
+int blr_profile_reset(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (int id = 0; id < K_COUNT; ++id) {
+        g_prof.counts[id] = 0;
+        g_prof.total_ms[id] = 0.0;
+    }
+    return BLR_OK;
+}
+
+}  // extern "C"

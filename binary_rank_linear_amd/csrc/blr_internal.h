@@ -1,0 +1,63 @@
+// Internal interface between the C ABI (blr_api.hip) and the kernels
+// (blr_kernels.hip). Not installed; the public interface is include/blr.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace blr {
+
+// Tiles of the MFMA contraction kernels (rows of the activation operand per
+// workgroup). The column reductions fused into the contractions write one
+// partial row per M tile.
+constexpr int GEMM_BM = 128;
+// Tokens per partial of the standalone column reduction.
+constexpr int COLSUM_ROWS = 64;
+
+// Kernel kinds, for per-kernel timing.
+enum KernelId {
+    K_EXPAND = 0,
+    K_GEMM_F1,   // a = (x.g) S_V
+    K_GEMM_F2,   // c = (a.l) S_U^T, y (+)= h.c
+    K_GEMM_B1,   // db = (dy.h.gs) S_U / gs, partials of dl
+    K_GEMM_B2,   // dx' = (db.l.gs) S_V^T / gs, dx (+)= g.dx', partials of dg
+    K_COLSUM,    // partials of dh = sum_t dy.c
+    K_FINISH,    // sum of partials into dh / dl / dg
+    K_COUNT
+};
+const char *kernel_name(int id);
+
+// out[m][n] = (sum_k f16(A[m][k] * colscale[k] * ascale) * B[n][k]) * oscale
+// with the f16 plane B [N][K]; every [M][N] array below has row stride N.
+struct GemmArgs {
+    const float *A;        // [M][lda] f32
+    int64_t lda;
+    const float *colscale; // [K]
+    float ascale;          // power of two
+    const uint16_t *B;     // f16 plane [N][K]
+    int64_t M;
+    int N, K;
+    float oscale;          // power of two (1/ascale)
+    float *out;            // [M][N] raw product (F1: tape a, F2: tape c, B1: db)
+    float *out2;           // [M][N] out2 (+)= out2col[n] * product (F2: y, B2: dx)
+    const float *out2col;
+    int out2acc;
+    const float *dot_other; // [M][N]: partial[mt][n] = sum_{m in tile} product * other
+    float *dot_partial;     // [ceil(M/GEMM_BM)][N]
+};
+
+enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_B1, GEMM_B2 };
+
+// Launchers: enqueue on `s`, return the launch error (hipSuccess if none).
+hipError_t launch_expand(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl, uint16_t *plt,
+                         hipStream_t s);
+hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s);
+hipError_t launch_colsum(const float *A, const float *B, int64_t M, int N, float *partial, hipStream_t s);
+hipError_t launch_finish(const float *partial, int64_t nparts, int N, float *out, hipStream_t s);
+
+// Profiling hooks around each launch (no-ops unless enabled).
+void prof_begin(int id, hipStream_t s);
+void prof_end(hipStream_t s);
+
+}  // namespace blr

@@ -1,0 +1,138 @@
+/*
+ * blr.h: C ABI of the binary low-rank (`blr`) linear layer on AMD Instinct
+ * MI355X (CDNA4, gfx950).
+ *
+ * The layer (cortiq-engine "src/gpu_wgpu/train_mm.rs", module doc block):
+ *
+ *     W^ = diag(h) . S_U . diag(l) . S_V^T . diag(g)
+ *
+ * with sign matrices S_U [d_out][r] and S_V [d_in][r] of +-1 stored as
+ * bitmaps, h [d_out], l [r] (the diagonal ell), g [d_in] in f32.
+ *
+ *   forward   a = (x.g) S_V        c = (a.l) S_U^T       y  = h.c  (or +=)
+ *   backward  dh += sum_t dy.c     db = (dy.h) S_U       dl += sum_t a.db
+ *             dx' = (db.l) S_V^T   dg += sum_t x.dx'     dx = g.dx' (or +=)
+ *
+ * Bitmaps (page: `expand` shader): row-major [rows][W] u32 words with
+ * W = ceil(r/32); bit j of word w is rank 32w+j; a set bit is +1, a clear
+ * bit -1. Bits at ranks >= r in the last word are ignored.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are HIP device pointers to row-major, contiguous
+ *     arrays. The caller owns every buffer. Inputs must not alias outputs.
+ *   - Shapes are int64. GPU-path rule (the page's GEMM contract: N a multiple
+ *     of 128, K of 32, activation rows padded to 128): d_in, d_out and r are
+ *     multiples of 128; the token count M is any value >= 1 (padding is
+ *     internal; exactly M rows are read and written).
+ *   - `stream` is a hipStream_t (passed as void*); NULL is the default
+ *     stream. Every call only enqueues work on it and returns without a host
+ *     synchronisation.
+ *   - Arguments are validated before anything is enqueued: on an error no
+ *     kernel is launched and no output is touched. Return value: BLR_OK or a
+ *     negative blr_status. A launch failure reported by the runtime after
+ *     validation returns BLR_ERR_HIP (earlier kernels of the call may have
+ *     run).
+ *   - The library never allocates device memory and never frees any; the
+ *     caller passes a device workspace of at least blr_workspace_bytes().
+ *     Two calls that share a workspace must be ordered (same stream).
+ *   - Arithmetic: operands of the four contractions are staged as f16 (round
+ *     to nearest even, subnormals kept, overflow gives +-inf) and multiplied
+ *     on the MFMA units with f32 accumulation; every reduction and every
+ *     output is f32. Results are deterministic: reruns give identical bits.
+ */
+#ifndef BLR_H
+#define BLR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BLR_OK = 0,
+    BLR_ERR_NULL = -1,      /* a required pointer is NULL */
+    BLR_ERR_SHAPE = -2,     /* a size is out of range or breaks the multiple-of-128 rule */
+    BLR_ERR_SCALE = -3,     /* gscale is not a positive finite power of two */
+    BLR_ERR_WORKSPACE = -4, /* workspace NULL or smaller than blr_workspace_bytes() */
+    BLR_ERR_DEVICE = -5,    /* current device is not gfx950 */
+    BLR_ERR_HIP = -6,       /* the HIP runtime reported an error */
+    BLR_ERR_ALIGN = -7      /* a pointer is not 16-byte aligned */
+} blr_status;
+
+/* Human-readable text of a status code (static storage). */
+const char *blr_status_string(int status);
+
+/* 1 when `hip_device` is a gfx950 device this library's kernels run on, 0
+ * otherwise (the page's `matrix_units` capability check). */
+int blr_device_supported(int hip_device);
+
+/* Bytes of device workspace blr_forward and blr_backward need for these
+ * sizes (the same figure serves both). 0 for invalid sizes. */
+size_t blr_workspace_bytes(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+
+/*
+ * Sign expansion (page: `expand` shader and its wrapper): bitmap
+ * bits [rows][ceil(r/32)] -> f16 planes
+ *     plane   [rows][r]   plane[i][k]   = S[i][k]   (0x3C00 = +1, 0xBC00 = -1)
+ *     plane_t [r][rows]   plane_t[k][i] = S[i][k]
+ * Either output may be NULL (not both). Any rows >= 1 and r >= 1 (no
+ * multiple-of-128 rule here). Bit-exact; writes exactly rows*r halves per
+ * plane. Output pointers must be 16-byte aligned; bits 4-byte aligned.
+ */
+int blr_expand_signs(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *plane, uint16_t *plane_t,
+                     void *stream);
+
+/*
+ * Forward (page: `blr_forward`, doc block forward line).
+ *   x [M][d_in]; bits_u [d_out][W]; bits_v [d_in][W]; h [d_out]; l [r]; g [d_in]
+ *   y [M][d_out]: accumulate_y = 0 writes y = h.c, 1 adds h.c to y (the page
+ *     overwrites for its first path and adds for later ones).
+ *   tape_a [M][r], tape_c [M][d_out]: receive a and c (f32), which
+ *     blr_backward reads; they must come from a forward on the same x and
+ *     parameters.
+ * Planes are expanded into the workspace on every call (the page re-expands
+ * per layer call). Float pointers must be 16-byte aligned.
+ */
+int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
+                const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y, int accumulate_y,
+                float *tape_a, float *tape_c, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward (page: `blr_backward`, doc block backward lines).
+ *   x [M][d_in] the forward's input; dy [M][d_out]; tape_a, tape_c from
+ *     blr_forward on the same x and parameters.
+ *   gscale: the power of two the gradients are staged under in f16 (dy.h
+ *     and db.l are multiplied by it before rounding to f16; the products are
+ *     divided by it in f32, exactly). Must be a positive finite power of two.
+ *   dh [d_out], dl [r], dg [d_in]: always accumulate (+=); zero them first
+ *     for a plain gradient.
+ *   dx [M][d_in]: accumulate_dx = 0 writes dx = g.dx', 1 adds.
+ * Float pointers must be 16-byte aligned.
+ */
+int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
+                 const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                 const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl, float *dg, float *dx,
+                 int accumulate_dx, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Per-kernel timing with HIP events (the role of the page's trainer
+ * profiling marks). blr_profile_enable(n) creates a pool of event pairs for
+ * up to n launches and brackets every later launch of this library with a
+ * pair on the launch's stream; blr_profile_enable(0) stops and releases the
+ * pool. blr_profile_read synchronises the recorded events, adds their
+ * durations into per-kernel totals, and copies up to `max` entries out:
+ * names[i] (static strings), counts[i] (launches), total_ms[i]. Returns the
+ * number of kernel kinds seen, or a negative status. blr_profile_reset
+ * clears the totals. These calls are not thread safe.
+ */
+int blr_profile_enable(int max_launches);
+int blr_profile_read(const char **names, int64_t *counts, double *total_ms, int max);
+int blr_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLR_H */

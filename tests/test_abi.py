@@ -1,0 +1,164 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/blr.h declares, sizes workspaces, and rejects bad arguments before
+touching the device (nothing is launched on any error path tested here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import binary_rank_linear_amd as blr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "blr.h")
+
+BLR_OK, E_NULL, E_SHAPE, E_SCALE, E_WS, E_DEV, E_HIP, E_ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(blr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("blr_forward", "blr_backward", "blr_expand_signs", "blr_workspace_bytes", "blr_status_string",
+              "blr_device_supported"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = blr.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", blr.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (blr_[a-z_]+)\b", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_is_gfx950_only():
+    """The offload bundle of our own build holds code for gfx950 only."""
+    data = open(blr.LIB_PATH, "rb").read()
+    arches = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", data))
+    assert arches == {b"gfx950"}, arches
+
+
+def test_status_strings():
+    for s in (BLR_OK, E_NULL, E_SHAPE, E_SCALE, E_WS, E_DEV, E_HIP, E_ALIGN):
+        assert blr.status_string(s) and blr.status_string(s) != "unknown status"
+    assert blr.status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert blr.blr_workspace_bytes(8192, 4096, 4096, 512) > 0
+    # planes (both orientations share one region per matrix) + db + partials
+    n = blr.blr_workspace_bytes(128, 256, 256, 128)
+    assert n >= 2 * 128 * (256 + 256) + 4 * 128 * 128
+    assert n % 256 == 0
+    assert blr.blr_workspace_bytes(30000, 5120, 17408, 2048) >= 4 * 30000 * 2048
+    for bad in [(0, 256, 256, 128), (128, 200, 256, 128), (128, 256, 100, 128), (128, 256, 256, 64), (-1, 256, 256, 128)]:
+        assert blr.blr_workspace_bytes(*bad) == 0
+
+
+class Fake:
+    """Aligned host buffers standing in for device pointers: every call
+    below fails validation before any device work, so they are never
+    dereferenced."""
+
+    def __init__(self):
+        self.keep = []
+
+    def __call__(self, nbytes=256, offset=0):
+        a = np.zeros(nbytes + 64, np.uint8)
+        self.keep.append(a)
+        base = a.ctypes.data
+        return ctypes.c_void_p(((base + 15) // 16) * 16 + offset)
+
+
+def fwd(lib, M, d_in, d_out, r, ptrs, ws_bytes=None):
+    ws_bytes = blr.blr_workspace_bytes(M, d_in, d_out, r) if ws_bytes is None else ws_bytes
+    return lib.blr_forward(M, d_in, d_out, r, ptrs["x"], ptrs["bu"], ptrs["bv"], ptrs["h"], ptrs["l"], ptrs["g"],
+                           ptrs["y"], 0, ptrs["ta"], ptrs["tc"], ptrs["ws"], ws_bytes, None)
+
+
+def bwd(lib, M, d_in, d_out, r, ptrs, gscale=1024.0, ws_bytes=None):
+    ws_bytes = blr.blr_workspace_bytes(M, d_in, d_out, r) if ws_bytes is None else ws_bytes
+    return lib.blr_backward(M, d_in, d_out, r, ptrs["x"], ptrs["dy"], ptrs["bu"], ptrs["bv"], ptrs["h"],
+                            ptrs["l"], ptrs["g"], ptrs["ta"], ptrs["tc"], ctypes.c_float(gscale), ptrs["dh"],
+                            ptrs["dl"], ptrs["dg"], ptrs["dx"], 0, ptrs["ws"], ws_bytes, None)
+
+
+KEYS = ["x", "dy", "bu", "bv", "h", "l", "g", "y", "ta", "tc", "dh", "dl", "dg", "dx", "ws"]
+
+
+@pytest.fixture
+def ptrs():
+    f = Fake()
+    d = {k: f() for k in KEYS}
+    d["_fake"] = f
+    return d
+
+
+def test_forward_rejects_null(ptrs):
+    lib = blr.load()
+    for k in ["x", "bu", "bv", "h", "l", "g", "y", "ta", "tc"]:
+        p = dict(ptrs)
+        p[k] = None
+        assert fwd(lib, 128, 256, 256, 128, p) == E_NULL, k
+
+
+def test_backward_rejects_null(ptrs):
+    lib = blr.load()
+    for k in ["x", "dy", "bu", "bv", "h", "l", "g", "ta", "tc", "dh", "dl", "dg", "dx"]:
+        p = dict(ptrs)
+        p[k] = None
+        assert bwd(lib, 128, 256, 256, 128, p) == E_NULL, k
+
+
+@pytest.mark.parametrize("shape", [(0, 256, 256, 128), (128, 200, 256, 128), (128, 256, 300, 128),
+                                   (128, 256, 256, 96), (128, 256, 256, 0), (-5, 256, 256, 128),
+                                   (128, 0, 256, 128)])
+def test_rejects_bad_shapes(ptrs, shape):
+    lib = blr.load()
+    assert fwd(lib, *shape, ptrs, ws_bytes=1 << 40) == E_SHAPE
+    assert bwd(lib, *shape, ptrs, ws_bytes=1 << 40) == E_SHAPE
+
+
+@pytest.mark.parametrize("gs", [0.0, -1024.0, 3.0, 1000.0, float("inf"), float("nan"), 1.5])
+def test_backward_rejects_bad_gscale(ptrs, gs):
+    assert bwd(blr.load(), 128, 256, 256, 128, ptrs, gscale=gs) == E_SCALE
+
+
+def test_rejects_small_workspace(ptrs):
+    lib = blr.load()
+    need = blr.blr_workspace_bytes(128, 256, 256, 128)
+    assert fwd(lib, 128, 256, 256, 128, ptrs, ws_bytes=need - 1) == E_WS
+    assert bwd(lib, 128, 256, 256, 128, ptrs, ws_bytes=need - 1) == E_WS
+    p = dict(ptrs)
+    p["ws"] = None
+    assert fwd(lib, 128, 256, 256, 128, p) == E_WS
+
+
+def test_rejects_misaligned(ptrs):
+    lib = blr.load()
+    f = ptrs["_fake"]
+    for k in ["x", "y", "ta", "h"]:
+        p = dict(ptrs)
+        p[k] = f(offset=4)
+        assert fwd(lib, 128, 256, 256, 128, p) == E_ALIGN, k
+    p = dict(ptrs)
+    p["dx"] = f(offset=8)
+    assert bwd(lib, 128, 256, 256, 128, p) == E_ALIGN
+
+
+def test_expand_rejects_bad_arguments(ptrs):
+    lib = blr.load()
+    f = ptrs["_fake"]
+    assert lib.blr_expand_signs(None, 4, 32, f(), f(), None) == E_NULL
+    assert lib.blr_expand_signs(f(), 4, 32, None, None, None) == E_NULL
+    assert lib.blr_expand_signs(f(), 0, 32, f(), None, None) == E_SHAPE
+    assert lib.blr_expand_signs(f(), 4, 0, None, f(), None) == E_SHAPE
+    assert lib.blr_expand_signs(f(), 4, 32, f(offset=2), None, None) == E_ALIGN

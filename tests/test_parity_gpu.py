@@ -1,0 +1,277 @@
+"""Forward + backward of the `blr` layer on the GPU (through the C ABI)
+against the f64 oracle on the same seeded inputs.
+
+Bar (test `blr_layer_matches_host` on the cortiq-engine train_mm.rs page):
+relative Frobenius error <= 3e-3 for y, dx, dh, dl, dg (and the tapes a, c).
+
+Small shapes run the oracle on every token and span several 128-row tiles
+with ragged tails. The full workload sizes run the GPU on all tokens, in the
+same launch configuration the benchmark times, and check
+  * a sample of tokens against the oracle: per-token outputs (y, a, c, dx)
+    depend only on that token, and with dy zero outside the sample the
+    column sums dh, dl, dg reduce to the sampled tokens exactly;
+  * whole-array properties: dx is exactly zero on every token whose dy is
+    zero, and with dense dy the Euler identities
+    sum(h.dh) = sum(l.dl) = sum(g.dg) = sum(x.dx) = sum(dy.y) hold.
+"""
+import numpy as np
+import pytest
+
+import binary_rank_linear_amd as blr
+import oracle
+import synth
+from _gpu_util import TOL, check_shapes_fit, host, say, to_dev
+
+
+def run_gpu(d, gscale, dev, y0=None, acc_y=False, grads0=None, dx0=None, acc_dx=False):
+    import torch
+    t = to_dev(d, dev)
+    y = None if y0 is None else torch.from_numpy(y0).to(dev)
+    y, ta, tc = blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], y=y, accumulate_y=acc_y)
+    kw = {}
+    if grads0 is not None:
+        kw = {k: torch.from_numpy(v).to(dev) for k, v in zip(("dh", "dl", "dg"), grads0)}
+    if dx0 is not None:
+        kw["dx"] = torch.from_numpy(dx0).to(dev)
+    dh, dl, dg, dx = blr.blr_backward(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
+                                      gscale, accumulate_dx=acc_dx, **kw)
+    torch.cuda.synchronize()
+    return {"y": host(y), "a": host(ta), "c": host(tc), "dh": host(dh), "dl": host(dl), "dg": host(dg),
+            "dx": host(dx)}
+
+
+def run_oracle(d, y0=None, acc_y=False, grads0=None, dx0=None, acc_dx=False):
+    y, a, c = oracle.forward(d["x"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"], y0=y0, accumulate=acc_y)
+    g0 = grads0 or (None, None, None)
+    dh, dl, dg, dx = oracle.backward(d["x"], d["dy"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"],
+                                     dh0=g0[0], dl0=g0[1], dg0=g0[2], dx0=dx0, accumulate_dx=acc_dx)
+    return {"y": y, "a": a, "c": c, "dh": dh, "dl": dl, "dg": dg, "dx": dx}
+
+
+def assert_close(got, want, keys=("y", "a", "c", "dh", "dl", "dg", "dx"), tol=TOL):
+    errs = {k: oracle.rel_frobenius(got[k], want[k]) for k in keys}
+    say("relative errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+    return errs
+
+
+SMALL = [
+    (128, 256, 256, 128),   # tiny workload shape
+    (70, 384, 256, 128),    # the page's test shape: 70 tokens (ragged), n=384, m=256
+    (300, 512, 384, 256),   # 2 full row tiles + 44-row tail
+    (1, 128, 128, 128),     # one token
+    (129, 256, 640, 384),   # one row past a tile
+    (513, 1024, 256, 512),  # wide d_in, tail of 1
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,d_in,d_out,r", SMALL)
+def test_small_shapes_match_oracle(dev, M, d_in, d_out, r):
+    check_shapes_fit(M, d_in, d_out, r)
+    d = synth.custom(M, d_in, d_out, r, seed=7000 + M, dy_sigma=1e-6, l_hi=0.1)
+    gs = float(d["gscale"])
+    say(f"small parity M={M} d_in={d_in} d_out={d_out} r={r} gscale={gs}")
+    assert_close(run_gpu(d, gs, dev), run_oracle(d))
+
+
+@pytest.mark.gpu
+def test_tiny_workload(dev):
+    w = synth.WORKLOADS[synth.SMALL]
+    d = synth.inputs(w)
+    say(f"workload {w.name}")
+    assert_close(run_gpu(d, w.gscale, dev), run_oracle(d))
+
+
+@pytest.mark.gpu
+def test_windows_workload_full_oracle(dev):
+    """M=2048, d=2048, r=256: small enough for the oracle on every token."""
+    w = synth.WORKLOADS["windows_2048x2048x2048_r256"]
+    d = synth.inputs(w)
+    say(f"workload {w.name} (full oracle)")
+    assert_close(run_gpu(d, w.gscale, dev), run_oracle(d))
+
+
+@pytest.mark.gpu
+def test_accumulate_flags(dev):
+    """y += h.c and dx += g.dx' when asked; dh, dl, dg always accumulate."""
+    M, d_in, d_out, r = 200, 256, 384, 128
+    d = synth.custom(M, d_in, d_out, r, seed=11, dy_sigma=1e-6)
+    R = np.random.default_rng(4)
+    y0 = R.standard_normal((M, d_out)).astype(np.float32)
+    dx0 = R.standard_normal((M, d_in)).astype(np.float32) * np.float32(1e-5)
+    g0 = tuple((R.standard_normal(n) * s).astype(np.float32) for n, s in ((d_out, 1e-4), (r, 1e-3), (d_in, 1e-4)))
+    gs = float(d["gscale"])
+    say("accumulate y and dx, nonzero dh/dl/dg")
+    got = run_gpu(d, gs, dev, y0=y0, acc_y=True, grads0=g0, dx0=dx0, acc_dx=True)
+    want = run_oracle(d, y0=y0, acc_y=True, grads0=g0, dx0=dx0, acc_dx=True)
+    assert_close(got, want)
+
+
+@pytest.mark.gpu
+def test_two_path_layer(dev):
+    """y = sum_p W^_p x over two paths, as the page's layer test: path 0
+    overwrites y and dx, path 1 adds (the page's `acc = pi > 0`), each path's
+    own dh/dl/dg; 70 tokens, m=256, n=384, r=128, gscale=1024."""
+    import torch
+    M, d_in, d_out, r = 70, 384, 256, 128
+    x = synth.normal((M, d_in), 1.0, 60)
+    dy = synth.normal((M, d_out), 1e-3, 61)
+    paths = [synth.params(synth.Workload("path", M, d_in, d_out, r, 1e-3, 1.0, False, 10 * (p + 1)))
+             for p in range(2)]
+    t = to_dev({"x": x, "dy": dy}, dev)
+    y = torch.empty((M, d_out), dtype=torch.float32, device=dev)
+    dx = torch.empty((M, d_in), dtype=torch.float32, device=dev)
+    tapes, grads = [], []
+    say("two-path forward/backward")
+    for p, pp in enumerate(paths):
+        tp = to_dev(pp, dev)
+        _, ta, tc = blr.blr_forward(t["x"], tp["bits_u"], tp["bits_v"], tp["h"], tp["l"], tp["g"], y=y,
+                                    accumulate_y=p > 0)
+        tapes.append((tp, ta, tc))
+    for p, (tp, ta, tc) in enumerate(tapes):
+        grads.append(blr.blr_backward(t["x"], t["dy"], tp["bits_u"], tp["bits_v"], tp["h"], tp["l"], tp["g"], ta,
+                                      tc, 1024.0, dx=dx, accumulate_dx=p > 0)[:3])
+    torch.cuda.synchronize()
+    wy = np.zeros((M, d_out))
+    wdx = np.zeros((M, d_in))
+    for p, pp in enumerate(paths):
+        wy, _, _ = oracle.forward(x, pp["bits_u"], pp["bits_v"], pp["h"], pp["l"], pp["g"], y0=wy, accumulate=True)
+        dh, dl, dg, wdx = oracle.backward(x, dy, pp["bits_u"], pp["bits_v"], pp["h"], pp["l"], pp["g"], dx0=wdx,
+                                          accumulate_dx=True)
+        got = {k: host(v) for k, v in zip(("dh", "dl", "dg"), grads[p])}
+        assert_close(got, {"dh": dh, "dl": dl, "dg": dg}, keys=("dh", "dl", "dg"))
+    assert_close({"y": host(y), "dx": host(dx)}, {"y": wy, "dx": wdx}, keys=("y", "dx"))
+
+
+@pytest.mark.gpu
+def test_deterministic_reruns(dev):
+    d = synth.custom(300, 512, 256, 128, seed=99, dy_sigma=1e-6)
+    gs = float(d["gscale"])
+    say("determinism: two identical runs")
+    a = run_gpu(d, gs, dev)
+    b = run_gpu(d, gs, dev)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.gpu
+def test_gscale_invariance_and_negative_control(dev):
+    """A power-of-two staging scale commutes with f16 rounding away from
+    under/overflow: results at 2^21 and 2^23 agree closely. At gscale 1 with
+    dy ~ N(0, 1e-7) the staged gradients sit in the f16 subnormals and the
+    error is far above the bar, so the scale is really applied."""
+    M, d_in, d_out, r = 256, 512, 512, 256
+    d = synth.custom(M, d_in, d_out, r, seed=5, dy_sigma=1e-7, l_hi=0.05)
+    want = run_oracle(d)
+    say("gscale 2^21 / 2^23 / 1")
+    g21 = run_gpu(d, 2.0 ** 21, dev)
+    g23 = run_gpu(d, 2.0 ** 23, dev)
+    g1 = run_gpu(d, 1.0, dev)
+    for k in ("dh", "dl", "dg", "dx"):
+        assert oracle.rel_frobenius(g21[k], g23[k]) < 1e-4, k
+    assert_close(g21, want)
+    bad = {k: oracle.rel_frobenius(g1[k], want[k]) for k in ("dl", "dg", "dx")}
+    say(f"gscale=1 errors {bad}")
+    assert all(v > 1e-2 for v in bad.values()), bad
+
+
+@pytest.mark.gpu
+def test_non_finite_values_propagate(dev):
+    """Overflow in staging gives inf, which reaches the outputs (no clamping):
+    the host can see it, as with the page's `sumsq` check."""
+    M, d_in, d_out, r = 128, 256, 256, 128
+    d = synth.custom(M, d_in, d_out, r, seed=3, dy_sigma=1.0)
+    say("non-finite: huge gscale and an inf input")
+    got = run_gpu(d, 2.0 ** 30, dev)  # dy*h*2^30 overflows f16
+    assert not np.all(np.isfinite(got["dx"])) and not np.all(np.isfinite(got["dl"]))
+    d2 = dict(d)
+    d2["x"] = d["x"].copy()
+    d2["x"][5, 7] = np.inf
+    got2 = run_gpu(d2, float(d["gscale"]), dev)
+    assert not np.all(np.isfinite(got2["y"][5]))
+    assert np.all(np.isfinite(got2["y"][np.arange(M) != 5]))
+
+
+@pytest.mark.gpu
+def test_writes_exactly_m_rows(dev):
+    """Outputs are views into larger buffers filled with a sentinel: the rows
+    past M (the internal padding to 128) are never written."""
+    import torch
+    M, d_in, d_out, r = 70, 256, 256, 128
+    d = synth.custom(M, d_in, d_out, r, seed=8, dy_sigma=1e-6)
+    t = to_dev(d, dev)
+    pad = 64
+    big = {k: torch.full((M + pad, n), 12345.0, device=dev) for k, n in (("y", d_out), ("a", r), ("c", d_out),
+                                                                          ("dx", d_in))}
+    say("row bounds: sentinel tails")
+    blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], y=big["y"][:M], tape_a=big["a"][:M],
+                    tape_c=big["c"][:M])
+    blr.blr_backward(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], big["a"][:M],
+                     big["c"][:M], float(d["gscale"]), dx=big["dx"][:M])
+    torch.cuda.synchronize()
+    for k, b in big.items():
+        tail = host(b[M:])
+        assert np.all(tail == 12345.0), k
+        assert np.all(np.isfinite(host(b[:M]))), k
+
+
+# ------------------------------------------------------------ full sizes --
+
+FULL = ["attn_proj_8192x4096x4096_r512", "mlp_up_8192x4096x12288_r1024", "mlp_down_8192x12288x4096_r1024",
+        "ragged_30000x5120x17408_r2048"]
+
+
+def sample_tokens(M: int, n: int = 48) -> np.ndarray:
+    R = np.random.default_rng(M)
+    s = set(R.choice(M, size=n - 3, replace=False).tolist())
+    s |= {0, M - 1, (M // 128) * 128 - 1}  # first, last (ragged tail), last of a full tile
+    return np.array(sorted(s))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_and_properties(dev, name):
+    import torch
+    w = synth.WORKLOADS[name]
+    check_shapes_fit(w.M, w.d_in, w.d_out, w.r)
+    d = synth.inputs(w)
+    S = sample_tokens(w.M)
+    t = to_dev(d, dev)
+    ws = blr.workspace(w.M, w.d_in, w.d_out, w.r, dev)
+    say(f"full size {name}: forward")
+    y, ta, tc = blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ws=ws)
+    # (1) dy zero outside the sample: the column sums reduce to the sample
+    dy_s = torch.zeros_like(t["dy"])
+    idx = torch.from_numpy(S).to(dev)
+    dy_s[idx] = t["dy"][idx]
+    say(f"full size {name}: backward with sampled dy")
+    dh, dl, dg, dx = blr.blr_backward(t["x"], dy_s, t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
+                                      w.gscale, ws=ws)
+    torch.cuda.synchronize()
+    sub = {k: d[k] for k in ("bits_u", "bits_v", "h", "l", "g")}
+    sub["x"], sub["dy"] = d["x"][S], d["dy"][S]
+    want = run_oracle(sub)
+    got = {"y": host(y[idx]), "a": host(ta[idx]), "c": host(tc[idx]), "dh": host(dh), "dl": host(dl),
+           "dg": host(dg), "dx": host(dx[idx])}
+    assert_close(got, want)
+    mask = torch.ones(w.M, dtype=torch.bool, device=dev)
+    mask[idx] = False
+    assert int(torch.count_nonzero(dx[mask])) == 0, "dx must be exactly zero where dy is zero"
+    # (2) dense dy: per-token dx on the sample, and the Euler identities
+    say(f"full size {name}: backward with dense dy")
+    dh, dl, dg, dx = blr.blr_backward(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
+                                      w.gscale, ws=ws)
+    torch.cuda.synchronize()
+    # dx of a token depends on that token's dy alone; sub["dy"] is the dense dy on the sample
+    want_dx = oracle.backward(sub["x"], sub["dy"], sub["bits_u"], sub["bits_v"], sub["h"], sub["l"], sub["g"])[3]
+    assert oracle.rel_frobenius(host(dx[idx]), want_dx) <= TOL
+    f64 = lambda v: v.double()
+    L = float((f64(t["dy"]) * f64(y)).sum())
+    for name_, theta, grad in (("h", t["h"], dh), ("l", t["l"], dl), ("g", t["g"], dg), ("x", t["x"], dx)):
+        terms = f64(theta) * f64(grad)
+        rss = float(torch.sqrt((terms * terms).sum()))
+        err = abs(float(terms.sum()) - L) / rss
+        say(f"Euler identity {name_}: sum={float(terms.sum()):.6e} L={L:.6e} normalised error {err:.2e}")
+        assert err <= TOL, name_
