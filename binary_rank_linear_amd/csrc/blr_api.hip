@@ -79,9 +79,9 @@ Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     L.part_h = off;
     off += up((size_t)(ceil_div(M, COLSUM_ROWS) * d_out) * 4);
     L.part_l = off;
-    off += up((size_t)(ceil_div(M, GEMM_BM) * r) * 4);
+    off += up((size_t)(ceil_div(M, GEMM_BM_MIN) * r) * 4);
     L.part_g = off;
-    off += up((size_t)(ceil_div(M, GEMM_BM) * d_in) * 4);
+    off += up((size_t)(ceil_div(M, GEMM_BM_MIN) * d_in) * 4);
     L.total = off;
     return L;
 }
@@ -94,7 +94,9 @@ bool shape_ok(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     if (d_in % 128 || d_out % 128 || r % 128) return false;
     const int64_t LIM = (int64_t)1 << 24;  // columns and ranks
     if (d_in > LIM || d_out > LIM || r > LIM) return false;
-    if (ceil_div(M, GEMM_BM) > 65535 || ceil_div(M, COLSUM_ROWS) > 65535) return false;
+    if (ceil_div(M, COLSUM_ROWS) > 65535) return false;
+    if ((d_out / 128) * ceil_div(M, GEMM_BM_MIN) > ((int64_t)1 << 31) - 1) return false;
+    if ((d_in / 128) * ceil_div(M, GEMM_BM_MIN) > ((int64_t)1 << 31) - 1) return false;
     return true;
 }
 
@@ -246,7 +248,8 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     float *part_l = (float *)(ws + L.part_l);
     float *part_g = (float *)(ws + L.part_g);
     const float inv = 1.0f / gscale;  // exact: gscale is a power of two
-    const int64_t mt = (M + GEMM_BM - 1) / GEMM_BM;
+    const int64_t mt_b1 = ceil_div(M, gemm_tile_rows(GEMM_B1));
+    const int64_t mt_b2 = ceil_div(M, gemm_tile_rows(GEMM_B2));
 
     BLR_TRY(launch_expand(bits_u, d_out, r, nullptr, plt_u, s));
     BLR_TRY(launch_expand(bits_v, d_in, r, pl_v, nullptr, s));
@@ -270,7 +273,7 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     b1.dot_other = tape_a;
     b1.dot_partial = part_l;
     BLR_TRY(launch_gemm(GEMM_B1, b1, s));
-    BLR_TRY(launch_finish(part_l, mt, (int)r, dl, s));
+    BLR_TRY(launch_finish(part_l, mt_b1, (int)r, dl, s));
 
     // dx' = f16(db.l.gs) S_V^T / gs; dx (+)= g.dx'; dg += sum_t x.dx'
     GemmArgs b2 = {};
@@ -289,7 +292,7 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     b2.dot_other = x;
     b2.dot_partial = part_g;
     BLR_TRY(launch_gemm(GEMM_B2, b2, s));
-    BLR_TRY(launch_finish(part_g, mt, (int)d_in, dg, s));
+    BLR_TRY(launch_finish(part_g, mt_b2, (int)d_in, dg, s));
     return BLR_OK;
 }
 

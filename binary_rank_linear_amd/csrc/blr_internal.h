@@ -8,10 +8,10 @@
 
 namespace blr {
 
-// Tiles of the MFMA contraction kernels (rows of the activation operand per
-// workgroup). The column reductions fused into the contractions write one
-// partial row per M tile.
-constexpr int GEMM_BM = 128;
+// Smallest row tile of the MFMA contraction kernels; the column reductions
+// fused into the contractions write one partial row per row tile, so the
+// partial buffers are sized for this tile.
+constexpr int GEMM_BM_MIN = 64;
 // Tokens per partial of the standalone column reduction.
 constexpr int COLSUM_ROWS = 64;
 
@@ -44,7 +44,7 @@ struct GemmArgs {
     const float *out2col;
     int out2acc;
     const float *dot_other; // [M][N]: partial[mt][n] = sum_{m in tile} product * other
-    float *dot_partial;     // [ceil(M/GEMM_BM)][N]
+    float *dot_partial;     // [ceil(M/gemm_tile_rows(kind))][N]
 };
 
 enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_B1, GEMM_B2 };
@@ -53,6 +53,7 @@ enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_B1, GEMM_B2 };
 hipError_t launch_expand(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl, uint16_t *plt,
                          hipStream_t s);
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s);
+int gemm_tile_rows(GemmKind kind);
 hipError_t launch_colsum(const float *A, const float *B, int64_t M, int N, float *partial, hipStream_t s);
 hipError_t launch_finish(const float *partial, int64_t nparts, int N, float *out, hipStream_t s);
 

@@ -15,6 +15,8 @@ namespace blr {
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // f16 bit patterns of +1 and -1.
 constexpr uint32_t F16_ONE = 0x3C00u;
@@ -104,15 +106,25 @@ hipError_t launch_expand(const uint32_t *bits, int64_t rows, int64_t r, uint16_t
 //   prod[m][n] = (sum_k f16(A[m][k] * colscale[k] * ascale) * B[n][k]) * oscale
 // B is an f16 sign plane [N][K]. Each workgroup computes a BM x BN tile with
 // WM x WN waves; each wave holds (BM/WM) x (BN/WN) f32 accumulators as
-// 32x32 MFMA tiles (v_mfma_f32_32x32x16_f16). The K loop is double
-// buffered through LDS: the next tile's global loads are in flight while the
-// current tile is multiplied.
+// 32x32 MFMA tiles (v_mfma_f32_32x32x16_f16).
+//
+// Memory pipeline: the activation operand streams from HBM, so each thread
+// keeps P K-stages of global loads in flight in registers (a ring of P
+// register sets). A stage is converted to f16 and written to one of two LDS
+// buffers one iteration before it is multiplied.
+//
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, each with its
+// own L2. The launch index is remapped so that consecutive tiles, which
+// share an activation row-block (the N tiles of one M tile), run on the
+// same XCD.
 //
 // MFMA 32x32x16 operand layout: lane l supplies row (l % 32) of A and column
 // (l % 32) of B, each with the 8 consecutive k of group (l / 32). The
 // accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4,
 // column l % 32.
-template <int BM, int BN, int BK, int WM, int WN, bool OUT, bool OUT2, bool DOT>
+constexpr int NUM_XCD = 8;
+
+template <int BM, int BN, int BK, int WM, int WN, int P, bool OUT, bool OUT2, bool DOT>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     constexpr int NT = WM * WN * 64;
     constexpr int LDK = BK + 8;  // halves per LDS row (pad: conflict-free 16-byte reads)
@@ -121,20 +133,65 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     constexpr int A_CHUNKS = BM * BK / 4;  // float4 chunks of an A tile
     constexpr int B_CHUNKS = BN * BK / 8;  // 16-byte chunks of a B tile
     constexpr int A_PER = A_CHUNKS / NT, B_PER = B_CHUNKS / NT;
+    constexpr int AROW_STEP = NT / (BK / 4);
     static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "tile/thread mismatch");
     static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "tile shape");
+    static_assert(NT % (BK / 4) == 0, "a thread keeps one column group of A");
+    static_assert(P % 2 == 0, "LDS buffer index must be static in the unrolled loop");
+    // Epilogue staging: each wave writes 32 accumulator rows x TN columns of
+    // f32 to its own LDS region, then reads them back as row-contiguous
+    // float4. Row stride EPS = TN + 8 floats puts the two half-waves (rows r
+    // and r+4) on disjoint banks.
+    constexpr int EPS = TN + 8;
+    constexpr int LANES_PER_ROW = TN / 4;
+    constexpr int ROWS_PER_READ = 64 / LANES_PER_ROW;
+    constexpr int LOOP_BYTES = 2 * (BM + BN) * LDK * 2;
+    constexpr int EPI_BYTES = (NT / 64) * 32 * EPS * 4;
+    constexpr int RED_BYTES = DOT ? WM * BN * 4 : 0;
+    constexpr int SMEM = LOOP_BYTES > EPI_BYTES + RED_BYTES ? LOOP_BYTES : EPI_BYTES + RED_BYTES;
+    static_assert(64 % LANES_PER_ROW == 0 && 32 % ROWS_PER_READ == 0, "epilogue read shape");
 
-    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * LDK];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+    _Float16 *As0 = reinterpret_cast<_Float16 *>(smem);
+    _Float16 *Bs0 = reinterpret_cast<_Float16 *>(smem + 2 * BM * LDK * 2);
+#define BLR_AS(buf) (As0 + (buf) * (BM * LDK))
+#define BLR_BS(buf) (Bs0 + (buf) * (BN * LDK))
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
-    const int nk = p.K / BK;
+    const int N = p.N, K = p.K;
+    const int ntn = N / BN;
+    const int L = blockIdx.x, G = gridDim.x;
+    const int T = (G % NUM_XCD == 0) ? (L % NUM_XCD) * (G / NUM_XCD) + L / NUM_XCD : L;
+    const int mt = T / ntn;
+    const int n0 = (T - mt * ntn) * BN;
+    const int64_t m0 = (int64_t)mt * BM;
+    const int nk = K / BK;  // a multiple of P (the launcher checks)
     const int64_t M = p.M;
-    const int N = p.N;
+
+    // Per-thread operand pointers, fixed for the whole K loop. Rows past M
+    // read row M-1 instead: a row of the product depends on its own A row
+    // only, and those rows are never stored or summed.
+    const int c4 = tid % (BK / 4);
+    const int arow = tid / (BK / 4);
+    const float *abase[A_PER];
+#pragma unroll
+    for (int v = 0; v < A_PER; ++v) {
+        int64_t gm = m0 + arow + v * AROW_STEP;
+        gm = gm < M ? gm : M - 1;
+        abase[v] = p.A + gm * p.lda + c4 * 4;
+    }
+    const float *cbase = p.colscale + c4 * 4;
+    const uint16_t *bbase[B_PER];
+    int bofs[B_PER];
+#pragma unroll
+    for (int v = 0; v < B_PER; ++v) {
+        const int idx = tid + v * NT;
+        const int row = idx / (BK / 8), c8 = idx % (BK / 8);
+        bbase[v] = p.B + (int64_t)(n0 + row) * K + c8 * 8;
+        bofs[v] = row * LDK + c8 * 8;
+    }
 
     f32x16_t acc[FM][FN];
 #pragma unroll
@@ -144,142 +201,165 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    float4 ar[A_PER];
-    uint4 br[B_PER];
+    f32x4_t ar[P][A_PER];
+    f32x4_t cr[P];
+    u32x4_t br[P][B_PER];
 
-    auto gload = [&](int kt) {
-        const int k0 = kt * BK;
-#pragma unroll
-        for (int v = 0; v < A_PER; ++v) {
-            const int idx = tid + v * NT;
-            const int row = idx / (BK / 4), c4 = idx % (BK / 4);
-            const int64_t gm = m0 + row;
-            if (gm < M)
-                ar[v] = *reinterpret_cast<const float4 *>(p.A + gm * p.lda + k0 + c4 * 4);
-            else
-                ar[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int v = 0; v < B_PER; ++v) {
-            const int idx = tid + v * NT;
-            const int row = idx / (BK / 8), c8 = idx % (BK / 8);
-            br[v] = *reinterpret_cast<const uint4 *>(p.B + (int64_t)(n0 + row) * p.K + k0 + c8 * 8);
-        }
-    };
-    auto sstore = [&](int kt, int buf) {
-        const int k0 = kt * BK;
-#pragma unroll
-        for (int v = 0; v < A_PER; ++v) {
-            const int idx = tid + v * NT;
-            const int row = idx / (BK / 4), c4 = idx % (BK / 4);
-            const float4 cs = *reinterpret_cast<const float4 *>(p.colscale + k0 + c4 * 4);
-            half4_t hv;
-            hv[0] = (_Float16)(ar[v].x * cs.x * p.ascale);
-            hv[1] = (_Float16)(ar[v].y * cs.y * p.ascale);
-            hv[2] = (_Float16)(ar[v].z * cs.z * p.ascale);
-            hv[3] = (_Float16)(ar[v].w * cs.w * p.ascale);
-            *reinterpret_cast<half4_t *>(&As[buf][row * LDK + c4 * 4]) = hv;
-        }
-#pragma unroll
-        for (int v = 0; v < B_PER; ++v) {
-            const int idx = tid + v * NT;
-            const int row = idx / (BK / 8), c8 = idx % (BK / 8);
-            *reinterpret_cast<uint4 *>(&Bs[buf][row * LDK + c8 * 8]) = br[v];
-        }
-    };
-    auto compute = [&](int buf) {
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            half8_t af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const half8_t *>(
-                    &As[buf][(wm * TM + i * 32 + (lane & 31)) * LDK + s * 16 + (lane >> 5) * 8]);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bf[j] = *reinterpret_cast<const half8_t *>(
-                    &Bs[buf][(wn * TN + j * 32 + (lane & 31)) * LDK + s * 16 + (lane >> 5) * 8]);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-    };
+#define BLR_GLOAD(q, kt)                                                                   \
+    do {                                                                                   \
+        const int k0_ = (kt) * BK;                                                         \
+        _Pragma("unroll") for (int v = 0; v < A_PER; ++v) ar[q][v] =                       \
+            *reinterpret_cast<const f32x4_t *>(abase[v] + k0_);                            \
+        cr[q] = *reinterpret_cast<const f32x4_t *>(cbase + k0_);                           \
+        _Pragma("unroll") for (int v = 0; v < B_PER; ++v) br[q][v] =                       \
+            *reinterpret_cast<const u32x4_t *>(bbase[v] + k0_);                            \
+    } while (0)
 
-    gload(0);
-    sstore(0, 0);
+#define BLR_SSTORE(q, buf)                                                                 \
+    do {                                                                                   \
+        const f32x4_t cs_ = cr[q];                                                         \
+        const float s_ = p.ascale;                                                         \
+        _Pragma("unroll") for (int v = 0; v < A_PER; ++v) {                                \
+            half4_t hv;                                                                    \
+            hv[0] = (_Float16)(ar[q][v].x * cs_.x * s_);                                   \
+            hv[1] = (_Float16)(ar[q][v].y * cs_.y * s_);                                   \
+            hv[2] = (_Float16)(ar[q][v].z * cs_.z * s_);                                   \
+            hv[3] = (_Float16)(ar[q][v].w * cs_.w * s_);                                   \
+            *reinterpret_cast<half4_t *>(BLR_AS(buf) + (arow + v * AROW_STEP) * LDK + c4 * 4) = hv; \
+        }                                                                                  \
+        _Pragma("unroll") for (int v = 0; v < B_PER; ++v)                                  \
+            *reinterpret_cast<u32x4_t *>(BLR_BS(buf) + bofs[v]) = br[q][v];                \
+    } while (0)
+
+#define BLR_COMPUTE(buf)                                                                   \
+    do {                                                                                   \
+        _Pragma("unroll") for (int s = 0; s < BK / 16; ++s) {                              \
+            half8_t af[FM], bf[FN];                                                        \
+            _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] =                         \
+                *reinterpret_cast<const half8_t *>(                                        \
+                    BLR_AS(buf) + (wm * TM + i * 32 + (lane & 31)) * LDK + s * 16 + (lane >> 5) * 8); \
+            _Pragma("unroll") for (int j = 0; j < FN; ++j) bf[j] =                         \
+                *reinterpret_cast<const half8_t *>(                                        \
+                    BLR_BS(buf) + (wn * TN + j * 32 + (lane & 31)) * LDK + s * 16 + (lane >> 5) * 8); \
+            _Pragma("unroll") for (int i = 0; i < FM; ++i)                                 \
+                _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] =                 \
+                    __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0); \
+        }                                                                                  \
+    } while (0)
+
+    // prologue: stages 0..P-1 in flight, stage 0 staged into LDS buffer 0
+#pragma unroll
+    for (int q = 0; q < P; ++q) BLR_GLOAD(q, q);
+    BLR_SSTORE(0, 0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        compute(cur);
-        if (kt + 1 < nk) sstore(kt + 1, cur ^ 1);
-        __syncthreads();
+    // steady state, unrolled by P so every register-set index is static:
+    // iteration kt issues stage kt+P into the set stage kt used, multiplies
+    // stage kt, then stages kt+1 into the other LDS buffer. Loads and stores
+    // are unconditional (stages past the end re-read the last stage and are
+    // never multiplied), so the compiler can count outstanding loads exactly
+    // and wait only for the stage it converts.
+    for (int kt0 = 0; kt0 < nk; kt0 += P) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int kt = kt0 + q;
+            BLR_GLOAD(q, kt + P < nk ? kt + P : nk - 1);
+            BLR_COMPUTE(q & 1);
+            BLR_SSTORE((q + 1) % P, (q + 1) & 1);
+            __syncthreads();
+            // keep the next stages' conversions out of this iteration: hoisted
+            // above the barrier they would wait for loads just issued
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+#undef BLR_GLOAD
+#undef BLR_SSTORE
+#undef BLR_COMPUTE
+#undef BLR_AS
+#undef BLR_BS
 
-    // Epilogue: products, tapes, scaled outputs and column partials.
-    float dotp[FN];
+    // Epilogue, one 32-row strip of the wave tile at a time: stage the
+    // accumulators through LDS, then each lane handles float4 column groups
+    // of whole rows: products, tapes, scaled outputs and column partials.
+    float *stage = reinterpret_cast<float *>(smem) + wave * 32 * EPS;
+    const int lr0 = lane / LANES_PER_ROW;
+    const int lc = (lane % LANES_PER_ROW) * 4;
+    const int gn = n0 + wn * TN + lc;
+    const bool full = m0 + BM <= M;
+    f32x4_t c2 = {0.f, 0.f, 0.f, 0.f};
+    if (OUT2) c2 = *reinterpret_cast<const f32x4_t *>(p.out2col + gn);
+    f32x4_t dsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < FN; ++j) dotp[j] = 0.0f;
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int gn = n0 + wn * TN + j * 32 + (lane & 31);
-        const float c2 = OUT2 ? p.out2col[gn] : 0.0f;
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+            for (int v = 0; v < 16; ++v)
+                stage[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EPS + j * 32 + (lane & 31)] = acc[i][j][v];
+        __syncthreads();
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int rin = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                const int64_t gm = m0 + rin;
-                if (gm < M) {
-                    const float val = acc[i][j][v] * p.oscale;
-                    const int64_t o = gm * N + gn;
-                    if (OUT) p.out[o] = val;
-                    if (OUT2) p.out2[o] = (p.out2acc ? p.out2[o] : 0.0f) + val * c2;
-                    if (DOT) dotp[j] += val * p.dot_other[o];
+        for (int it = 0; it < 32 / ROWS_PER_READ; ++it) {
+            const int lr = it * ROWS_PER_READ + lr0;
+            const int64_t gm = m0 + wm * TM + i * 32 + lr;
+            f32x4_t val = *reinterpret_cast<const f32x4_t *>(stage + lr * EPS + lc);
+            val *= p.oscale;
+            if (full || gm < M) {
+                const int64_t o = gm * N + gn;
+                if (OUT) *reinterpret_cast<f32x4_t *>(p.out + o) = val;
+                if (OUT2) {
+                    f32x4_t y = val * c2;
+                    if (p.out2acc) y = *reinterpret_cast<const f32x4_t *>(p.out2 + o) + y;
+                    *reinterpret_cast<f32x4_t *>(p.out2 + o) = y;
                 }
+                if (DOT) dsum += val * *reinterpret_cast<const f32x4_t *>(p.dot_other + o);
             }
         }
+        __syncthreads();
     }
     if (DOT) {
-        // rows of a column are spread over the two lane halves and the WM
-        // waves of a column strip: fold lanes l and l+32, then waves in order
-        float *red = reinterpret_cast<float *>(&As[0][0]);  // [WM][BN], K loop is done
+        // lanes with the same columns (l mod LANES_PER_ROW) fold in a fixed
+        // butterfly, then the WM waves of a column strip add in wave order
 #pragma unroll
-        for (int j = 0; j < FN; ++j) dotp[j] += __shfl_xor(dotp[j], 32);
-        if (lane < 32) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) red[wm * BN + wn * TN + j * 32 + lane] = dotp[j];
+        for (int off = LANES_PER_ROW; off < 64; off <<= 1) {
+            dsum.x += __shfl_xor(dsum.x, off);
+            dsum.y += __shfl_xor(dsum.y, off);
+            dsum.z += __shfl_xor(dsum.z, off);
+            dsum.w += __shfl_xor(dsum.w, off);
         }
+        float *red = reinterpret_cast<float *>(smem + EPI_BYTES);  // [WM][BN]
+        if (lane < LANES_PER_ROW) *reinterpret_cast<f32x4_t *>(red + wm * BN + wn * TN + lc) = dsum;
         __syncthreads();
         for (int c = tid; c < BN; c += NT) {
             float s = 0.0f;
 #pragma unroll
             for (int w = 0; w < WM; ++w) s += red[w * BN + c];
-            p.dot_partial[(int64_t)blockIdx.y * N + n0 + c] = s;
+            p.dot_partial[(int64_t)mt * N + n0 + c] = s;
         }
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool OUT, bool OUT2, bool DOT>
+template <int BM, int BN, int BK, int WM, int WN, int P, bool OUT, bool OUT2, bool DOT>
 static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
-    static_assert(BM == GEMM_BM, "partials are laid out per GEMM_BM tile");
-    static_assert(WM * BN * 4 <= 2 * BM * (BK + 8) * 2, "reduction buffer fits in the A tiles");
-    dim3 grid((unsigned)(a.N / BN), (unsigned)((a.M + BM - 1) / BM));
+    if (a.N % BN != 0 || a.K % (BK * P) != 0 || a.K / BK < P) return hipErrorInvalidValue;
+    const int64_t tiles = (int64_t)(a.N / BN) * ((a.M + BM - 1) / BM);
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WM, WN, OUT, OUT2, DOT>), grid, dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WM, WN, P, OUT, OUT2, DOT>), dim3((unsigned)tiles),
+                       dim3(WM * WN * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
 }
 
+// Row tiles per kind. F1/B1 (N = r, long K) use 64-row tiles so a launch has
+// 2 workgroups per CU at the headline size; F2/B2 (N = d_out or d_in) use
+// 128-row tiles.
+int gemm_tile_rows(GemmKind kind) { return (kind == GEMM_F1 || kind == GEMM_B1) ? 64 : 128; }
+
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     switch (kind) {
-        case GEMM_F1: return launch_gemm_t<128, 128, 32, 2, 2, true, false, false>(K_GEMM_F1, a, s);
-        case GEMM_F2: return launch_gemm_t<128, 128, 32, 2, 2, true, true, false>(K_GEMM_F2, a, s);
-        case GEMM_B1: return launch_gemm_t<128, 128, 32, 2, 2, true, false, true>(K_GEMM_B1, a, s);
-        case GEMM_B2: return launch_gemm_t<128, 128, 32, 2, 2, false, true, true>(K_GEMM_B2, a, s);
+        case GEMM_F1: return launch_gemm_t<64, 128, 32, 2, 2, 4, true, false, false>(K_GEMM_F1, a, s);
+        case GEMM_F2: return launch_gemm_t<128, 128, 32, 2, 2, 4, true, true, false>(K_GEMM_F2, a, s);
+        case GEMM_B1: return launch_gemm_t<64, 128, 32, 2, 2, 4, true, false, true>(K_GEMM_B1, a, s);
+        case GEMM_B2: return launch_gemm_t<128, 128, 32, 2, 2, 4, false, true, true>(K_GEMM_B2, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -288,7 +368,8 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
 // Column reduction (page: `colsum_prod`, one thread per column with a serial
 // row loop, later two-pass): here each thread owns 4 adjacent columns
 // (float4, so a wavefront reads 1 KB contiguous per row) over COLSUM_ROWS
-// tokens; partial[chunk][col] is summed in chunk order by finish_kernel.
+// tokens, 4 rows per step; partial[chunk][col] is summed in chunk order by
+// finish_kernel.
 __global__ __launch_bounds__(256) void colsum_prod_kernel(const float *__restrict__ A, const float *__restrict__ B,
                                                           int64_t M, int N, float *__restrict__ partial) {
     const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -296,7 +377,23 @@ __global__ __launch_bounds__(256) void colsum_prod_kernel(const float *__restric
     const int64_t t0 = (int64_t)blockIdx.y * COLSUM_ROWS;
     const int64_t t1 = t0 + COLSUM_ROWS < M ? t0 + COLSUM_ROWS : M;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t t = t0; t < t1; ++t) {
+    int64_t t = t0;
+    for (; t + 4 <= t1; t += 4) {
+        float4 a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            a[u] = *reinterpret_cast<const float4 *>(A + (t + u) * N + col);
+            b[u] = *reinterpret_cast<const float4 *>(B + (t + u) * N + col);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            s.x += a[u].x * b[u].x;
+            s.y += a[u].y * b[u].y;
+            s.z += a[u].z * b[u].z;
+            s.w += a[u].w * b[u].w;
+        }
+    }
+    for (; t < t1; ++t) {
         const float4 a = *reinterpret_cast<const float4 *>(A + t * N + col);
         const float4 b = *reinterpret_cast<const float4 *>(B + t * N + col);
         s.x += a.x * b.x;
@@ -316,19 +413,35 @@ hipError_t launch_colsum(const float *A, const float *B, int64_t M, int N, float
     return e;
 }
 
-// out[n] += sum over parts (in order) of partial[part][n].
+// out[n] += sum over parts of partial[part][n]. A workgroup owns 64
+// columns; its 4 waves take every 4th part (in order), then the 4 wave sums
+// are added in wave order: a fixed order, so results are deterministic.
 __global__ __launch_bounds__(256) void finish_kernel(const float *__restrict__ partial, int64_t nparts, int N,
                                                      float *__restrict__ out) {
-    const int col = blockIdx.x * 256 + threadIdx.x;
-    if (col >= N) return;
+    __shared__ float red[4][64];
+    const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int col = blockIdx.x * 64 + c;
     float s = 0.0f;
-    for (int64_t q = 0; q < nparts; ++q) s += partial[q * N + col];
-    out[col] = out[col] + s;
+    if (col < N) {
+        int64_t pi = q;
+        for (; pi + 12 < nparts; pi += 16) {
+            const float v0 = partial[pi * N + col], v1 = partial[(pi + 4) * N + col];
+            const float v2 = partial[(pi + 8) * N + col], v3 = partial[(pi + 12) * N + col];
+            s += v0;
+            s += v1;
+            s += v2;
+            s += v3;
+        }
+        for (; pi < nparts; pi += 4) s += partial[pi * N + col];
+    }
+    red[q][c] = s;
+    __syncthreads();
+    if (q == 0 && col < N) out[col] = out[col] + (((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
 }
 
 hipError_t launch_finish(const float *partial, int64_t nparts, int N, float *out, hipStream_t s) {
     prof_begin(K_FINISH, s);
-    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, partial, nparts, N, out);
+    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s, partial, nparts, N, out);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
