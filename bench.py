@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0     # HBM3E
 RIDGE = PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
 
 
-def kernel_work(name: str, w: synth.Workload) -> tuple[float, float]:
+def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[float, float]:
     """Algorithmic (bytes, flops) of one launch of a kernel: the bytes each
     kernel must move between HBM and the chip at minimum (f32 activations,
     f16 sign planes read once) and the MFMA flops of its contraction."""
@@ -39,8 +39,10 @@ def kernel_work(name: str, w: synth.Workload) -> tuple[float, float]:
     f32, f16 = 4, 2
     if name == "gemm_f1_xg_sv":      # read x, write tape a, plane [r][d_in]
         return M * (di + r) * f32 + r * di * f16 + di * f32, 2.0 * M * r * di
-    if name == "gemm_f2_al_sut":     # read a, write tape c and y, plane [d_out][r]
-        return M * (r + 2 * do) * f32 + do * r * f16 + (r + do) * f32, 2.0 * M * do * r
+    if name == "gemm_f2_al_sut":     # read a, write y (and the c tape), plane [d_out][r]
+        return M * (r + (2 if keep_c else 1) * do) * f32 + do * r * f16 + (r + do) * f32, 2.0 * M * do * r
+    if name == "gemm_dh_recompute_c":  # read a and dy, plane [d_out][r]; dh partials are negligible
+        return M * (r + do) * f32 + do * r * f16 + r * f32, 2.0 * M * do * r
     if name == "gemm_b1_dyh_su":     # read dy and a, write db, plane [r][d_out]
         return M * (do + 2 * r) * f32 + r * do * f16 + do * f32, 2.0 * M * r * do
     if name == "gemm_b2_dbl_svt":    # read db and x, write dx, plane [d_in][r]
@@ -92,6 +94,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--keep-c", action="store_true",
+                    help="store the f32 c tape in the forward (the page's layout) instead of recomputing c")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer's data-parallel split and its "
@@ -112,7 +116,7 @@ def main():
     M, di, do, r = w.M, w.d_in, w.d_out, w.r
     y = torch.empty((M, do), dtype=torch.float32, device=dev)
     ta = torch.empty((M, r), dtype=torch.float32, device=dev)
-    tc = torch.empty((M, do), dtype=torch.float32, device=dev)
+    tc = torch.empty((M, do), dtype=torch.float32, device=dev) if args.keep_c else None
     dx = torch.empty((M, di), dtype=torch.float32, device=dev)
     dh = torch.zeros(do, dtype=torch.float32, device=dev)
     dl = torch.zeros(r, dtype=torch.float32, device=dev)
@@ -169,12 +173,12 @@ def main():
     kernels = {}
     for name, (count, tot_ms) in prof.items():
         avg_us = 1000.0 * tot_ms / count
-        nbytes, flops = kernel_work(name, w)
+        nbytes, flops = kernel_work(name, w, args.keep_c)
         kernels[name] = {"launches_per_step": count / args.steps, "avg_us": round(avg_us, 3),
                          "gbs": round(nbytes / (avg_us * 1e-6) / 1e9, 1) if nbytes else None,
                          "tflops": round(flops / (avg_us * 1e-6) / 1e12, 1) if flops else None}
     dom = max(prof, key=lambda k: prof[k][1])
-    nbytes, flops = kernel_work(dom, w)
+    nbytes, flops = kernel_work(dom, w, args.keep_c)
     avg_s = prof[dom][1] / prof[dom][0] / 1000.0
     if flops and flops / nbytes > RIDGE:
         roof = {"bound": "mfma", "achieved": round(flops / avg_s / 1e12, 2), "peak": PEAK_F16_TFLOPS,
@@ -203,7 +207,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "d_in": di, "d_out": do, "r": r, "gscale": w.gscale,
-                   "accumulate": "f32", "paths": 1},
+                   "accumulate": "f32", "paths": 1, "c_tape": "f32" if args.keep_c else "recomputed"},
         "tflops_metric": round(tf_metric, 2),
         "pct_f16_peak_metric": round(100 * tf_metric / PEAK_F16_TFLOPS, 2),
         "tflops_mfma": round(tf_mfma, 2),

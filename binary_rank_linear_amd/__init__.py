@@ -134,9 +134,11 @@ def blr_expand_signs(bits, rows: int, r: int, plane=True, plane_t=True, stream=N
 
 
 def blr_forward(x, bits_u, bits_v, h, l, g, *, y=None, accumulate_y=False, tape_a=None, tape_c=None,
-                ws=None, stream=None):
+                keep_c=False, ws=None, stream=None):
     """Forward of one path. Returns (y, tape_a, tape_c); outputs not given
-    are allocated. y is overwritten unless accumulate_y."""
+    are allocated. y is overwritten unless accumulate_y. The c tape is kept
+    only when tape_c is given or keep_c is set; otherwise tape_c is None and
+    blr_backward recomputes c."""
     import torch
     f32 = (torch.float32,)
     M, d_in = _need(x, "x", f32).shape
@@ -149,7 +151,9 @@ def blr_forward(x, bits_u, bits_v, h, l, g, *, y=None, accumulate_y=False, tape_
     y = torch.empty((M, d_out), dtype=torch.float32, device=dev) if y is None else _need(y, "y", f32, (M, d_out))
     tape_a = torch.empty((M, r), dtype=torch.float32, device=dev) if tape_a is None else \
         _need(tape_a, "tape_a", f32, (M, r))
-    tape_c = torch.empty((M, d_out), dtype=torch.float32, device=dev) if tape_c is None else \
+    if tape_c is None and keep_c:
+        tape_c = torch.empty((M, d_out), dtype=torch.float32, device=dev)
+    if tape_c is not None:
         _need(tape_c, "tape_c", f32, (M, d_out))
     if ws is None:
         ws = workspace(M, d_in, d_out, r, dev)
@@ -162,7 +166,8 @@ def blr_forward(x, bits_u, bits_v, h, l, g, *, y=None, accumulate_y=False, tape_
 def blr_backward(x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale: float, *, dh=None, dl=None, dg=None,
                  dx=None, accumulate_dx=False, ws=None, stream=None):
     """Backward of one path. dh/dl/dg accumulate (allocated as zeros when not
-    given); dx is overwritten unless accumulate_dx. Returns (dh, dl, dg, dx)."""
+    given); dx is overwritten unless accumulate_dx. tape_c is the forward's
+    c tape, or None when the forward kept none. Returns (dh, dl, dg, dx)."""
     import torch
     f32 = (torch.float32,)
     M, d_in = _need(x, "x", f32).shape
@@ -173,7 +178,8 @@ def blr_backward(x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale: float, 
     _need(bits_u, "bits_u", _bits_dtypes(), (d_out, W))
     _need(bits_v, "bits_v", _bits_dtypes(), (d_in, W))
     _need(tape_a, "tape_a", f32, (M, r))
-    _need(tape_c, "tape_c", f32, (M, d_out))
+    if tape_c is not None:
+        _need(tape_c, "tape_c", f32, (M, d_out))
     dev = x.device
     dh = torch.zeros(d_out, dtype=torch.float32, device=dev) if dh is None else _need(dh, "dh", f32, (d_out,))
     dl = torch.zeros(r, dtype=torch.float32, device=dev) if dl is None else _need(dl, "dl", f32, (r,))

@@ -60,6 +60,7 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
     size_t plane_u, plane_v;  // f16 planes (one orientation each per call)
+    size_t plane_u2;          // S_U [d_out][r] when the backward recomputes c
     size_t db;                // f32 [M][r]
     size_t part_h, part_l, part_g;
     size_t total;
@@ -74,6 +75,8 @@ Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     off += up((size_t)(d_out * r) * 2);
     L.plane_v = off;
     off += up((size_t)(d_in * r) * 2);
+    L.plane_u2 = off;
+    off += up((size_t)(d_out * r) * 2);
     L.db = off;
     off += up((size_t)(M * r) * 4);
     L.part_h = off;
@@ -92,8 +95,9 @@ Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
 bool shape_ok(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     if (M < 1 || d_in < 128 || d_out < 128 || r < 128) return false;
     if (d_in % 128 || d_out % 128 || r % 128) return false;
-    const int64_t LIM = (int64_t)1 << 24;  // columns and ranks
-    if (d_in > LIM || d_out > LIM || r > LIM) return false;
+    const int64_t LIM = (int64_t)1 << 24;  // ranks
+    if (r > LIM) return false;
+    if ((d_in + 63) / 64 > 65535 || (d_out + 63) / 64 > 65535) return false;  // expansion grid rows
     if (ceil_div(M, COLSUM_ROWS) > 65535) return false;
     if ((d_out / 128) * ceil_div(M, GEMM_BM_MIN) > ((int64_t)1 << 31) - 1) return false;
     if ((d_in / 128) * ceil_div(M, GEMM_BM_MIN) > ((int64_t)1 << 31) - 1) return false;
@@ -166,17 +170,20 @@ int blr_expand_signs(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl
     if (!aligned4(bits) || (plane && !aligned16(plane)) || (plane_t && !aligned16(plane_t))) return BLR_ERR_ALIGN;
     int st = current_device_ok();
     if (st != BLR_OK) return st;
-    return launch_expand(bits, rows, r, plane, plane_t, (hipStream_t)stream) == hipSuccess ? BLR_OK : BLR_ERR_HIP;
+    ExpandJobs jobs = {};
+    jobs.job[0] = {bits, rows, r, plane, plane_t};
+    jobs.count = 1;
+    return launch_expand(jobs, (hipStream_t)stream) == hipSuccess ? BLR_OK : BLR_ERR_HIP;
 }
 
 int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
                 const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y, int accumulate_y,
                 float *tape_a, float *tape_c, void *workspace, size_t workspace_bytes, void *stream) {
-    if (!x || !bits_u || !bits_v || !h || !l || !g || !y || !tape_a || !tape_c) return BLR_ERR_NULL;
+    if (!x || !bits_u || !bits_v || !h || !l || !g || !y || !tape_a) return BLR_ERR_NULL;
     if (!shape_ok(M, d_in, d_out, r)) return BLR_ERR_SHAPE;
     const Layout L = layout(M, d_in, d_out, r);
     if (workspace == nullptr || workspace_bytes < L.total) return BLR_ERR_WORKSPACE;
-    const void *f16a[] = {x, h, l, g, y, tape_a, tape_c, workspace};
+    const void *f16a[] = {x, h, l, g, y, tape_a, tape_c ? tape_c : tape_a, workspace};
     for (const void *p : f16a)
         if (!aligned16(p)) return BLR_ERR_ALIGN;
     if (!aligned4(bits_u) || !aligned4(bits_v)) return BLR_ERR_ALIGN;
@@ -188,8 +195,11 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
     uint16_t *plt_v = (uint16_t *)(ws + L.plane_v);  // S_V^T [r][d_in]
     uint16_t *pl_u = (uint16_t *)(ws + L.plane_u);   // S_U   [d_out][r]
 
-    BLR_TRY(launch_expand(bits_v, d_in, r, nullptr, plt_v, s));
-    BLR_TRY(launch_expand(bits_u, d_out, r, pl_u, nullptr, s));
+    ExpandJobs ex = {};
+    ex.job[0] = {bits_v, d_in, r, nullptr, plt_v};
+    ex.job[1] = {bits_u, d_out, r, pl_u, nullptr};
+    ex.count = 2;
+    BLR_TRY(launch_expand(ex, s));
 
     GemmArgs f1 = {};
     f1.A = x;
@@ -218,7 +228,7 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
     f2.out2 = y;
     f2.out2col = h;
     f2.out2acc = accumulate_y ? 1 : 0;
-    BLR_TRY(launch_gemm(GEMM_F2, f2, s));
+    BLR_TRY(launch_gemm(tape_c ? GEMM_F2 : GEMM_F2_NOTAPE, f2, s));
     return BLR_OK;
 }
 
@@ -226,13 +236,13 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
                  const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
                  const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl, float *dg, float *dx,
                  int accumulate_dx, void *workspace, size_t workspace_bytes, void *stream) {
-    if (!x || !dy || !bits_u || !bits_v || !h || !l || !g || !tape_a || !tape_c || !dh || !dl || !dg || !dx)
+    if (!x || !dy || !bits_u || !bits_v || !h || !l || !g || !tape_a || !dh || !dl || !dg || !dx)
         return BLR_ERR_NULL;
     if (!shape_ok(M, d_in, d_out, r)) return BLR_ERR_SHAPE;
     if (!pow2_scale_ok(gscale)) return BLR_ERR_SCALE;
     const Layout L = layout(M, d_in, d_out, r);
     if (workspace == nullptr || workspace_bytes < L.total) return BLR_ERR_WORKSPACE;
-    const void *f16a[] = {x, dy, h, l, g, tape_a, tape_c, dh, dl, dg, dx, workspace};
+    const void *f16a[] = {x, dy, h, l, g, tape_a, tape_c ? tape_c : tape_a, dh, dl, dg, dx, workspace};
     for (const void *p : f16a)
         if (!aligned16(p)) return BLR_ERR_ALIGN;
     if (!aligned4(bits_u) || !aligned4(bits_v)) return BLR_ERR_ALIGN;
@@ -251,12 +261,35 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     const int64_t mt_b1 = ceil_div(M, gemm_tile_rows(GEMM_B1));
     const int64_t mt_b2 = ceil_div(M, gemm_tile_rows(GEMM_B2));
 
-    BLR_TRY(launch_expand(bits_u, d_out, r, nullptr, plt_u, s));
-    BLR_TRY(launch_expand(bits_v, d_in, r, pl_v, nullptr, s));
+    uint16_t *pl_u = (uint16_t *)(ws + L.plane_u2);   // S_U   [d_out][r]
+    ExpandJobs ex = {};
+    ex.job[0] = {bits_u, d_out, r, tape_c ? nullptr : pl_u, plt_u};
+    ex.job[1] = {bits_v, d_in, r, pl_v, nullptr};
+    ex.count = 2;
+    BLR_TRY(launch_expand(ex, s));
 
-    // dh += sum_t dy.c
-    BLR_TRY(launch_colsum(dy, tape_c, M, (int)d_out, part_h, s));
-    BLR_TRY(launch_finish(part_h, (M + COLSUM_ROWS - 1) / COLSUM_ROWS, (int)d_out, dh, s));
+    // partials of dh = sum_t dy.c: from the stored tape, or with c
+    // recomputed by F2's contraction (same tiles, so the same c)
+    int64_t nparts_h;
+    if (tape_c) {
+        BLR_TRY(launch_colsum(dy, tape_c, M, (int)d_out, part_h, s));
+        nparts_h = ceil_div(M, COLSUM_ROWS);
+    } else {
+        GemmArgs rc = {};
+        rc.A = tape_a;
+        rc.lda = r;
+        rc.colscale = l;
+        rc.ascale = 1.0f;
+        rc.B = pl_u;
+        rc.M = M;
+        rc.N = (int)d_out;
+        rc.K = (int)r;
+        rc.oscale = 1.0f;
+        rc.dot_other = dy;
+        rc.dot_partial = part_h;
+        BLR_TRY(launch_gemm(GEMM_DH, rc, s));
+        nparts_h = ceil_div(M, gemm_tile_rows(GEMM_DH));
+    }
 
     // db = f16(dy.h.gs) S_U / gs; dl += sum_t a.db
     GemmArgs b1 = {};
@@ -273,7 +306,6 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     b1.dot_other = tape_a;
     b1.dot_partial = part_l;
     BLR_TRY(launch_gemm(GEMM_B1, b1, s));
-    BLR_TRY(launch_finish(part_l, mt_b1, (int)r, dl, s));
 
     // dx' = f16(db.l.gs) S_V^T / gs; dx (+)= g.dx'; dg += sum_t x.dx'
     GemmArgs b2 = {};
@@ -292,7 +324,14 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     b2.dot_other = x;
     b2.dot_partial = part_g;
     BLR_TRY(launch_gemm(GEMM_B2, b2, s));
-    BLR_TRY(launch_finish(part_g, mt_b2, (int)d_in, dg, s));
+
+    // dh, dl, dg += their partial sums, one launch
+    FinishJobs fin = {};
+    fin.job[0] = {part_h, nparts_h, (int)d_out, dh};
+    fin.job[1] = {part_l, mt_b1, (int)r, dl};
+    fin.job[2] = {part_g, mt_b2, (int)d_in, dg};
+    fin.count = 3;
+    BLR_TRY(launch_finish(fin, s));
     return BLR_OK;
 }
 

@@ -22,7 +22,8 @@ enum KernelId {
     K_GEMM_F2,   // c = (a.l) S_U^T, y (+)= h.c
     K_GEMM_B1,   // db = (dy.h.gs) S_U / gs, partials of dl
     K_GEMM_B2,   // dx' = (db.l.gs) S_V^T / gs, dx (+)= g.dx', partials of dg
-    K_COLSUM,    // partials of dh = sum_t dy.c
+    K_COLSUM,    // partials of dh = sum_t dy.c from the stored c tape
+    K_GEMM_DH,   // c recomputed as in F2, partials of dh = sum_t dy.c
     K_FINISH,    // sum of partials into dh / dl / dg
     K_COUNT
 };
@@ -47,15 +48,41 @@ struct GemmArgs {
     float *dot_partial;     // [ceil(M/gemm_tile_rows(kind))][N]
 };
 
-enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_B1, GEMM_B2 };
+// F2 writes the c tape and y (F2) or y only (F2_NOTAPE); DH repeats F2's
+// contraction with the same tiles (so c is bit-identical) and sums dy.c.
+enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_F2_NOTAPE, GEMM_B1, GEMM_B2, GEMM_DH };
+
+// Sign-plane expansion jobs (one bitmap each; pl and/or plt may be null).
+struct ExpandJob {
+    const uint32_t *bits;  // [rows][ceil(r/32)]
+    int64_t rows, r;
+    uint16_t *pl;   // f16 [rows][r]
+    uint16_t *plt;  // f16 [r][rows]
+};
+struct ExpandJobs {
+    ExpandJob job[2];
+    int count;
+};
+
+// Column-sum finishing jobs: out[n] += sum_p partial[p][n].
+struct FinishJob {
+    const float *partial;
+    int64_t nparts;
+    int N;
+    float *out;
+};
+struct FinishJobs {
+    FinishJob job[3];
+    int blocks_before[3];
+    int count;
+};
 
 // Launchers: enqueue on `s`, return the launch error (hipSuccess if none).
-hipError_t launch_expand(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl, uint16_t *plt,
-                         hipStream_t s);
+hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s);
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s);
 int gemm_tile_rows(GemmKind kind);
 hipError_t launch_colsum(const float *A, const float *B, int64_t M, int N, float *partial, hipStream_t s);
-hipError_t launch_finish(const float *partial, int64_t nparts, int N, float *out, hipStream_t s);
+hipError_t launch_finish(FinishJobs jobs, hipStream_t s);
 
 // Profiling hooks around each launch (no-ops unless enabled).
 void prof_begin(int id, hipStream_t s);

@@ -31,17 +31,22 @@ __device__ __forceinline__ uint32_t sign_pair(uint32_t b0, uint32_t b1) {
 // Sign expansion (page: `expand` shader). One workgroup decodes a tile of
 // 64 rows x 64 ranks: the 128 words go through LDS, then both planes are
 // written with 32-byte row segments (the page writes the transposed plane
-// one strided half at a time).
+// one strided half at a time). One launch serves up to two bitmaps
+// (blockIdx.z picks the job).
 constexpr int EXP_TR = 64;
 constexpr int EXP_TK = 64;
 
-__global__ __launch_bounds__(256) void expand_signs_kernel(const uint32_t *__restrict__ bits, int64_t rows,
-                                                           int64_t r, int64_t W, uint16_t *__restrict__ pl,
-                                                           uint16_t *__restrict__ plt) {
-    __shared__ uint32_t wb[EXP_TR][2];
-    const int t = threadIdx.x;
+__global__ __launch_bounds__(256) void expand_signs_kernel(ExpandJobs jobs) {
+    const ExpandJob &jb = jobs.job[blockIdx.z];
+    const int64_t rows = jb.rows, r = jb.r, W = (jb.r + 31) / 32;
+    const uint32_t *__restrict__ bits = jb.bits;
+    uint16_t *__restrict__ pl = jb.pl;
+    uint16_t *__restrict__ plt = jb.plt;
     const int64_t r0 = (int64_t)blockIdx.y * EXP_TR;
     const int64_t k0 = (int64_t)blockIdx.x * EXP_TK;
+    if (r0 >= rows || k0 >= r) return;  // this job's grid is smaller than the launch's
+    __shared__ uint32_t wb[EXP_TR][2];
+    const int t = threadIdx.x;
     const int64_t w0 = k0 >> 5;
     if (t < 2 * EXP_TR) {
         const int row = t >> 1, wi = t & 1;
@@ -89,12 +94,16 @@ __global__ __launch_bounds__(256) void expand_signs_kernel(const uint32_t *__res
     }
 }
 
-hipError_t launch_expand(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl, uint16_t *plt,
-                         hipStream_t s) {
-    const int64_t W = (r + 31) / 32;
-    dim3 grid((unsigned)((r + EXP_TK - 1) / EXP_TK), (unsigned)((rows + EXP_TR - 1) / EXP_TR));
+hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s) {
+    int64_t gx = 1, gy = 1;
+    for (int j = 0; j < jobs.count; ++j) {
+        const int64_t x = (jobs.job[j].r + EXP_TK - 1) / EXP_TK, y = (jobs.job[j].rows + EXP_TR - 1) / EXP_TR;
+        gx = x > gx ? x : gx;
+        gy = y > gy ? y : gy;
+    }
     prof_begin(K_EXPAND, s);
-    hipLaunchKernelGGL(expand_signs_kernel, grid, dim3(256), 0, s, bits, rows, r, W, pl, plt);
+    hipLaunchKernelGGL(expand_signs_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)jobs.count), dim3(256), 0, s,
+                       jobs);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
@@ -124,7 +133,7 @@ hipError_t launch_expand(const uint32_t *bits, int64_t rows, int64_t r, uint16_t
 // column l % 32.
 constexpr int NUM_XCD = 8;
 
-template <int BM, int BN, int BK, int WM, int WN, int P, bool OUT, bool OUT2, bool DOT>
+template <int BM, int BN, int BK, int WM, int WN, int P, bool OUT, bool OUT2, bool DOT, int GM>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     constexpr int NT = WM * WN * 64;
     constexpr int LDK = BK + 8;  // halves per LDS row (pad: conflict-free 16-byte reads)
@@ -164,8 +173,22 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     const int ntn = N / BN;
     const int L = blockIdx.x, G = gridDim.x;
     const int T = (G % NUM_XCD == 0) ? (L % NUM_XCD) * (G / NUM_XCD) + L / NUM_XCD : L;
-    const int mt = T / ntn;
-    const int n0 = (T - mt * ntn) * BN;
+    // Within an XCD's run of tiles, GM consecutive M tiles share an N tile:
+    // the workgroups resident at one time then read a few activation
+    // row-blocks and a few plane slices, which fit in the XCD's L2. GM = 1
+    // walks the N tiles of one M tile first.
+    int mt, nt;
+    if (GM == 1) {
+        mt = T / ntn;
+        nt = T - mt * ntn;
+    } else {
+        const int mtiles = (int)((p.M + BM - 1) / BM);
+        const int grp = T / (GM * ntn), within = T - grp * (GM * ntn);
+        const int gsz = (grp + 1) * GM <= mtiles ? GM : mtiles - grp * GM;
+        mt = grp * GM + within % gsz;
+        nt = within / gsz;
+    }
+    const int n0 = nt * BN;
     const int64_t m0 = (int64_t)mt * BM;
     const int nk = K / BK;  // a multiple of P (the launcher checks)
     const int64_t M = p.M;
@@ -280,6 +303,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     // Epilogue, one 32-row strip of the wave tile at a time: stage the
     // accumulators through LDS, then each lane handles float4 column groups
     // of whole rows: products, tapes, scaled outputs and column partials.
+    constexpr int RPT = 32 / ROWS_PER_READ;  // row reads per strip per lane
     float *stage = reinterpret_cast<float *>(smem) + wave * 32 * EPS;
     const int lr0 = lane / LANES_PER_ROW;
     const int lc = (lane % LANES_PER_ROW) * 4;
@@ -287,9 +311,32 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     const bool full = m0 + BM <= M;
     f32x4_t c2 = {0.f, 0.f, 0.f, 0.f};
     if (OUT2) c2 = *reinterpret_cast<const f32x4_t *>(p.out2col + gn);
+    // The column-sum operand streams from HBM once: issue every load of this
+    // lane's rows now (rows past M read row M-1 and are not used), so their
+    // latencies overlap instead of following one another.
+    f32x4_t pre[DOT ? FM : 1][DOT ? RPT : 1];
+    if (DOT) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int it = 0; it < RPT; ++it) {
+                int64_t gm = m0 + wm * TM + i * 32 + it * ROWS_PER_READ + lr0;
+                gm = gm < M ? gm : M - 1;
+                pre[i][it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p.dot_other + gm * N + gn));
+            }
+    }
     f32x4_t dsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        f32x4_t old[OUT2 ? RPT : 1];
+        if (OUT2 && p.out2acc) {
+#pragma unroll
+            for (int it = 0; it < RPT; ++it) {
+                int64_t gm = m0 + wm * TM + i * 32 + it * ROWS_PER_READ + lr0;
+                gm = gm < M ? gm : M - 1;
+                old[it] = *reinterpret_cast<const f32x4_t *>(p.out2 + gm * N + gn);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -297,7 +344,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
                 stage[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EPS + j * 32 + (lane & 31)] = acc[i][j][v];
         __syncthreads();
 #pragma unroll
-        for (int it = 0; it < 32 / ROWS_PER_READ; ++it) {
+        for (int it = 0; it < RPT; ++it) {
             const int lr = it * ROWS_PER_READ + lr0;
             const int64_t gm = m0 + wm * TM + i * 32 + lr;
             f32x4_t val = *reinterpret_cast<const f32x4_t *>(stage + lr * EPS + lc);
@@ -307,10 +354,10 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
                 if (OUT) *reinterpret_cast<f32x4_t *>(p.out + o) = val;
                 if (OUT2) {
                     f32x4_t y = val * c2;
-                    if (p.out2acc) y = *reinterpret_cast<const f32x4_t *>(p.out2 + o) + y;
+                    if (p.out2acc) y = old[it] + y;
                     *reinterpret_cast<f32x4_t *>(p.out2 + o) = y;
                 }
-                if (DOT) dsum += val * *reinterpret_cast<const f32x4_t *>(p.dot_other + o);
+                if (DOT) dsum += val * pre[i][it];
             }
         }
         __syncthreads();
@@ -337,29 +384,40 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int P, bool OUT, bool OUT2, bool DOT>
+template <int BM, int BN, int BK, int WM, int WN, int P, bool OUT, bool OUT2, bool DOT, int GM>
 static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
     if (a.N % BN != 0 || a.K % (BK * P) != 0 || a.K / BK < P) return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)(a.N / BN) * ((a.M + BM - 1) / BM);
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WM, WN, P, OUT, OUT2, DOT>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WM, WN, P, OUT, OUT2, DOT, GM>), dim3((unsigned)tiles),
                        dim3(WM * WN * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
 }
 
-// Row tiles per kind. F1/B1 (N = r, long K) use 64-row tiles so a launch has
-// 2 workgroups per CU at the headline size; F2/B2 (N = d_out or d_in) use
-// 128-row tiles.
-int gemm_tile_rows(GemmKind kind) { return (kind == GEMM_F1 || kind == GEMM_B1) ? 64 : 128; }
+// Tile shapes per kind (tuned at the headline size M=8192, d=4096, r=512).
+// F1/B1 (N = r, long K): 128x128 tiles; B1 runs 8 waves of 32x64. F2/B2
+// (N = d_out or d_in, K = r): 128x256 tiles of 8 waves, grouped tile order.
+int gemm_tile_rows(GemmKind) { return 128; }
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
+    const bool wide = a.N % 256 == 0;
     switch (kind) {
-        case GEMM_F1: return launch_gemm_t<64, 128, 32, 2, 2, 4, true, false, false>(K_GEMM_F1, a, s);
-        case GEMM_F2: return launch_gemm_t<128, 128, 32, 2, 2, 4, true, true, false>(K_GEMM_F2, a, s);
-        case GEMM_B1: return launch_gemm_t<64, 128, 32, 2, 2, 4, true, false, true>(K_GEMM_B1, a, s);
-        case GEMM_B2: return launch_gemm_t<128, 128, 32, 2, 2, 4, false, true, true>(K_GEMM_B2, a, s);
+        case GEMM_F1: return launch_gemm_t<128, 128, 32, 2, 2, 4, true, false, false, 1>(K_GEMM_F1, a, s);
+        case GEMM_F2:
+            if (wide) return launch_gemm_t<128, 256, 32, 2, 4, 4, true, true, false, 8>(K_GEMM_F2, a, s);
+            return launch_gemm_t<128, 128, 32, 2, 2, 4, true, true, false, 8>(K_GEMM_F2, a, s);
+        case GEMM_F2_NOTAPE:
+            if (wide) return launch_gemm_t<128, 256, 32, 2, 4, 4, false, true, false, 8>(K_GEMM_F2, a, s);
+            return launch_gemm_t<128, 128, 32, 2, 2, 4, false, true, false, 8>(K_GEMM_F2, a, s);
+        case GEMM_DH:
+            if (wide) return launch_gemm_t<128, 256, 32, 2, 4, 4, false, false, true, 8>(K_GEMM_DH, a, s);
+            return launch_gemm_t<128, 128, 32, 2, 2, 4, false, false, true, 8>(K_GEMM_DH, a, s);
+        case GEMM_B1: return launch_gemm_t<128, 128, 32, 4, 2, 4, true, false, true, 1>(K_GEMM_B1, a, s);
+        case GEMM_B2:
+            if (wide) return launch_gemm_t<128, 256, 32, 2, 4, 4, false, true, true, 8>(K_GEMM_B2, a, s);
+            return launch_gemm_t<128, 128, 32, 2, 2, 4, false, true, true, 8>(K_GEMM_B2, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -368,40 +426,29 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
 // Column reduction (page: `colsum_prod`, one thread per column with a serial
 // row loop, later two-pass): here each thread owns 4 adjacent columns
 // (float4, so a wavefront reads 1 KB contiguous per row) over COLSUM_ROWS
-// tokens, 4 rows per step; partial[chunk][col] is summed in chunk order by
-// finish_kernel.
+// tokens, 8 rows per step (16 loads in flight); partial[chunk][col] is
+// summed in chunk order by finish_kernel.
 __global__ __launch_bounds__(256) void colsum_prod_kernel(const float *__restrict__ A, const float *__restrict__ B,
                                                           int64_t M, int N, float *__restrict__ partial) {
     const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (col >= N) return;
     const int64_t t0 = (int64_t)blockIdx.y * COLSUM_ROWS;
     const int64_t t1 = t0 + COLSUM_ROWS < M ? t0 + COLSUM_ROWS : M;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
     int64_t t = t0;
-    for (; t + 4 <= t1; t += 4) {
-        float4 a[4], b[4];
+    for (; t + 8 <= t1; t += 8) {
+        f32x4_t a[8], b[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[u] = *reinterpret_cast<const float4 *>(A + (t + u) * N + col);
-            b[u] = *reinterpret_cast<const float4 *>(B + (t + u) * N + col);
+        for (int u = 0; u < 8; ++u) {
+            a[u] = *reinterpret_cast<const f32x4_t *>(A + (t + u) * N + col);
+            b[u] = *reinterpret_cast<const f32x4_t *>(B + (t + u) * N + col);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            s.x += a[u].x * b[u].x;
-            s.y += a[u].y * b[u].y;
-            s.z += a[u].z * b[u].z;
-            s.w += a[u].w * b[u].w;
-        }
+        for (int u = 0; u < 8; ++u) s += a[u] * b[u];
     }
-    for (; t < t1; ++t) {
-        const float4 a = *reinterpret_cast<const float4 *>(A + t * N + col);
-        const float4 b = *reinterpret_cast<const float4 *>(B + t * N + col);
-        s.x += a.x * b.x;
-        s.y += a.y * b.y;
-        s.z += a.z * b.z;
-        s.w += a.w * b.w;
-    }
-    *reinterpret_cast<float4 *>(partial + (int64_t)blockIdx.y * N + col) = s;
+    for (; t < t1; ++t)
+        s += *reinterpret_cast<const f32x4_t *>(A + t * N + col) * *reinterpret_cast<const f32x4_t *>(B + t * N + col);
+    *reinterpret_cast<f32x4_t *>(partial + (int64_t)blockIdx.y * N + col) = s;
 }
 
 hipError_t launch_colsum(const float *A, const float *B, int64_t M, int N, float *partial, hipStream_t s) {
@@ -413,14 +460,20 @@ hipError_t launch_colsum(const float *A, const float *B, int64_t M, int N, float
     return e;
 }
 
-// out[n] += sum over parts of partial[part][n]. A workgroup owns 64
-// columns; its 4 waves take every 4th part (in order), then the 4 wave sums
-// are added in wave order: a fixed order, so results are deterministic.
-__global__ __launch_bounds__(256) void finish_kernel(const float *__restrict__ partial, int64_t nparts, int N,
-                                                     float *__restrict__ out) {
+// out[n] += sum over parts of partial[part][n], for up to three vectors in
+// one launch (each workgroup owns 64 columns of one job; its 4 waves take
+// every 4th part in order, then the 4 wave sums are added in wave order: a
+// fixed order, so results are deterministic).
+__global__ __launch_bounds__(256) void finish_kernel(FinishJobs jobs) {
     __shared__ float red[4][64];
+    int b = blockIdx.x, j = 0;
+    while (j + 1 < jobs.count && b >= jobs.blocks_before[j + 1]) ++j;
+    const FinishJob &jb = jobs.job[j];
+    const float *__restrict__ partial = jb.partial;
+    const int64_t nparts = jb.nparts;
+    const int N = jb.N;
     const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
-    const int col = blockIdx.x * 64 + c;
+    const int col = (b - jobs.blocks_before[j]) * 64 + c;
     float s = 0.0f;
     if (col < N) {
         int64_t pi = q;
@@ -436,12 +489,17 @@ __global__ __launch_bounds__(256) void finish_kernel(const float *__restrict__ p
     }
     red[q][c] = s;
     __syncthreads();
-    if (q == 0 && col < N) out[col] = out[col] + (((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
+    if (q == 0 && col < N) jb.out[col] = jb.out[col] + (((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
 }
 
-hipError_t launch_finish(const float *partial, int64_t nparts, int N, float *out, hipStream_t s) {
+hipError_t launch_finish(FinishJobs jobs, hipStream_t s) {
+    int total = 0;
+    for (int j = 0; j < jobs.count; ++j) {
+        jobs.blocks_before[j] = total;
+        total += (jobs.job[j].N + 63) / 64;
+    }
     prof_begin(K_FINISH, s);
-    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s, partial, nparts, N, out);
+    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)total), dim3(256), 0, s, jobs);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
@@ -455,6 +513,7 @@ const char *kernel_name(int id) {
         case K_GEMM_B1: return "gemm_b1_dyh_su";
         case K_GEMM_B2: return "gemm_b2_dbl_svt";
         case K_COLSUM: return "colsum_dy_c";
+        case K_GEMM_DH: return "gemm_dh_recompute_c";
         case K_FINISH: return "colsum_finish";
     }
     return "?";

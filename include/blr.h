@@ -89,9 +89,12 @@ int blr_expand_signs(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl
  *   x [M][d_in]; bits_u [d_out][W]; bits_v [d_in][W]; h [d_out]; l [r]; g [d_in]
  *   y [M][d_out]: accumulate_y = 0 writes y = h.c, 1 adds h.c to y (the page
  *     overwrites for its first path and adds for later ones).
- *   tape_a [M][r], tape_c [M][d_out]: receive a and c (f32), which
- *     blr_backward reads; they must come from a forward on the same x and
- *     parameters.
+ *   tape_a [M][r]: receives a (f32), which blr_backward reads.
+ *   tape_c [M][d_out] or NULL: receives c (f32) when given (the page keeps
+ *     c for its backward). When NULL, c is not stored and blr_backward
+ *     recomputes it with the same contraction (bit-identical c): 2*M*r*d_out
+ *     more MFMA flops instead of 8*M*d_out bytes of HBM traffic.
+ *   The tapes must come from a forward on the same x and parameters.
  * Planes are expanded into the workspace on every call (the page re-expands
  * per layer call). Float pointers must be 16-byte aligned.
  */
@@ -101,8 +104,9 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
 
 /*
  * Backward (page: `blr_backward`, doc block backward lines).
- *   x [M][d_in] the forward's input; dy [M][d_out]; tape_a, tape_c from
- *     blr_forward on the same x and parameters.
+ *   x [M][d_in] the forward's input; dy [M][d_out]; tape_a and tape_c from
+ *     blr_forward on the same x and parameters; tape_c NULL exactly when
+ *     the forward stored none (then c is recomputed from tape_a).
  *   gscale: the power of two the gradients are staged under in f16 (dy.h
  *     and db.l are multiplied by it before rounding to f16; the products are
  *     divided by it in f32, exactly). Must be a positive finite power of two.

@@ -104,7 +104,7 @@ def ptrs():
 
 def test_forward_rejects_null(ptrs):
     lib = blr.load()
-    for k in ["x", "bu", "bv", "h", "l", "g", "y", "ta", "tc"]:
+    for k in ["x", "bu", "bv", "h", "l", "g", "y", "ta"]:
         p = dict(ptrs)
         p[k] = None
         assert fwd(lib, 128, 256, 256, 128, p) == E_NULL, k
@@ -112,7 +112,7 @@ def test_forward_rejects_null(ptrs):
 
 def test_backward_rejects_null(ptrs):
     lib = blr.load()
-    for k in ["x", "dy", "bu", "bv", "h", "l", "g", "ta", "tc", "dh", "dl", "dg", "dx"]:
+    for k in ["x", "dy", "bu", "bv", "h", "l", "g", "ta", "dh", "dl", "dg", "dx"]:
         p = dict(ptrs)
         p[k] = None
         assert bwd(lib, 128, 256, 256, 128, p) == E_NULL, k
