@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--keep-c", action="store_true",
                     help="store the f32 c tape in the forward (the page's layout) instead of recomputing c")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before the run, copy a buffer of this many MiB three times with torch (a plain copy "
+                         "kernel of known traffic, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer's data-parallel split and its "
@@ -108,6 +111,13 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     blr.load()
     if not blr.device_supported(0):
         raise SystemExit("cuda:0 is not gfx950")

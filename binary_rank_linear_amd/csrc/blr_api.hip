@@ -59,9 +59,8 @@ constexpr size_t ALIGN = 256;
 size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t plane_u, plane_v;  // f16 planes (one orientation each per call)
-    size_t plane_u2;          // S_U [d_out][r] when the backward recomputes c
-    size_t db;                // f32 [M][r]
+    size_t bits_t;  // transposed bitmap [r][max(d_in, d_out)/32] (u32)
+    size_t db;      // f32 [M][r]
     size_t part_h, part_l, part_g;
     size_t total;
 };
@@ -71,12 +70,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     Layout L;
     size_t off = 0;
-    L.plane_u = off;
-    off += up((size_t)(d_out * r) * 2);
-    L.plane_v = off;
-    off += up((size_t)(d_in * r) * 2);
-    L.plane_u2 = off;
-    off += up((size_t)(d_out * r) * 2);
+    L.bits_t = off;
+    off += up((size_t)(r * ((d_in > d_out ? d_in : d_out) / 32)) * 4);
     L.db = off;
     off += up((size_t)(M * r) * 4);
     L.part_h = off;
@@ -99,6 +94,9 @@ bool shape_ok(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     if (r > LIM) return false;
     if ((d_in + 63) / 64 > 65535 || (d_out + 63) / 64 > 65535) return false;  // expansion grid rows
     if (ceil_div(M, COLSUM_ROWS) > 65535) return false;
+    // the contraction kernels address every operand with 32-bit byte offsets
+    const int64_t widest = d_in > d_out ? (d_in > r ? d_in : r) : (d_out > r ? d_out : r);
+    if (M * widest * 4 > (int64_t)0xFFFFFFFF) return false;
     if ((d_out / 128) * ceil_div(M, GEMM_BM_MIN) > ((int64_t)1 << 31) - 1) return false;
     if ((d_in / 128) * ceil_div(M, GEMM_BM_MIN) > ((int64_t)1 << 31) - 1) return false;
     return true;
@@ -192,21 +190,15 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
 
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
-    uint16_t *plt_v = (uint16_t *)(ws + L.plane_v);  // S_V^T [r][d_in]
-    uint16_t *pl_u = (uint16_t *)(ws + L.plane_u);   // S_U   [d_out][r]
-
-    ExpandJobs ex = {};
-    ex.job[0] = {bits_v, d_in, r, nullptr, plt_v};
-    ex.job[1] = {bits_u, d_out, r, pl_u, nullptr};
-    ex.count = 2;
-    BLR_TRY(launch_expand(ex, s));
+    uint32_t *bits_vt = (uint32_t *)(ws + L.bits_t);  // S_V^T as a bitmap [r][d_in/32]
+    BLR_TRY(launch_transpose_bits(bits_v, d_in, r, bits_vt, s));
 
     GemmArgs f1 = {};
     f1.A = x;
     f1.lda = d_in;
     f1.colscale = g;
     f1.ascale = 1.0f;
-    f1.B = plt_v;
+    f1.Bbits = bits_vt;
     f1.M = M;
     f1.N = (int)r;
     f1.K = (int)d_in;
@@ -219,7 +211,7 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
     f2.lda = r;
     f2.colscale = l;
     f2.ascale = 1.0f;
-    f2.B = pl_u;
+    f2.Bbits = bits_u;
     f2.M = M;
     f2.N = (int)d_out;
     f2.K = (int)r;
@@ -251,8 +243,7 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
 
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
-    uint16_t *plt_u = (uint16_t *)(ws + L.plane_u);  // S_U^T [r][d_out]
-    uint16_t *pl_v = (uint16_t *)(ws + L.plane_v);   // S_V   [d_in][r]
+    uint32_t *bits_ut = (uint32_t *)(ws + L.bits_t);  // S_U^T as a bitmap [r][d_out/32]
     float *db = (float *)(ws + L.db);
     float *part_h = (float *)(ws + L.part_h);
     float *part_l = (float *)(ws + L.part_l);
@@ -261,12 +252,7 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     const int64_t mt_b1 = ceil_div(M, gemm_tile_rows(GEMM_B1));
     const int64_t mt_b2 = ceil_div(M, gemm_tile_rows(GEMM_B2));
 
-    uint16_t *pl_u = (uint16_t *)(ws + L.plane_u2);   // S_U   [d_out][r]
-    ExpandJobs ex = {};
-    ex.job[0] = {bits_u, d_out, r, tape_c ? nullptr : pl_u, plt_u};
-    ex.job[1] = {bits_v, d_in, r, pl_v, nullptr};
-    ex.count = 2;
-    BLR_TRY(launch_expand(ex, s));
+    BLR_TRY(launch_transpose_bits(bits_u, d_out, r, bits_ut, s));
 
     // partials of dh = sum_t dy.c: from the stored tape, or with c
     // recomputed by F2's contraction (same tiles, so the same c)
@@ -280,7 +266,7 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
         rc.lda = r;
         rc.colscale = l;
         rc.ascale = 1.0f;
-        rc.B = pl_u;
+        rc.Bbits = bits_u;
         rc.M = M;
         rc.N = (int)d_out;
         rc.K = (int)r;
@@ -297,7 +283,7 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     b1.lda = d_out;
     b1.colscale = h;
     b1.ascale = gscale;
-    b1.B = plt_u;
+    b1.Bbits = bits_ut;
     b1.M = M;
     b1.N = (int)r;
     b1.K = (int)d_out;
@@ -313,7 +299,7 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     b2.lda = r;
     b2.colscale = l;
     b2.ascale = gscale;
-    b2.B = pl_v;
+    b2.Bbits = bits_v;
     b2.M = M;
     b2.N = (int)d_in;
     b2.K = (int)r;

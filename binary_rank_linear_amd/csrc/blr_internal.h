@@ -18,6 +18,7 @@ constexpr int COLSUM_ROWS = 64;
 // Kernel kinds, for per-kernel timing.
 enum KernelId {
     K_EXPAND = 0,
+    K_TRANSPOSE, // bitmap [rows][r/32] -> [r][rows/32]
     K_GEMM_F1,   // a = (x.g) S_V
     K_GEMM_F2,   // c = (a.l) S_U^T, y (+)= h.c
     K_GEMM_B1,   // db = (dy.h.gs) S_U / gs, partials of dl
@@ -29,14 +30,15 @@ enum KernelId {
 };
 const char *kernel_name(int id);
 
-// out[m][n] = (sum_k f16(A[m][k] * colscale[k] * ascale) * B[n][k]) * oscale
-// with the f16 plane B [N][K]; every [M][N] array below has row stride N.
+// out[m][n] = (sum_k f16(A[m][k] * colscale[k] * ascale) * S[n][k]) * oscale
+// with the +-1 plane S [N][K] given as a bitmap; every [M][N] array below
+// has row stride N.
 struct GemmArgs {
     const float *A;        // [M][lda] f32
     int64_t lda;
     const float *colscale; // [K]
     float ascale;          // power of two
-    const uint16_t *B;     // f16 plane [N][K]
+    const uint32_t *Bbits; // sign bitmap of the plane [N][K]: row n, word k/32, bit k%32 (set = +1)
     int64_t M;
     int N, K;
     float oscale;          // power of two (1/ascale)
@@ -79,6 +81,9 @@ struct FinishJobs {
 
 // Launchers: enqueue on `s`, return the launch error (hipSuccess if none).
 hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s);
+// out [r][rows/32]: bit (i % 32) of word i / 32 in row k is rank k of row i
+// of bits [rows][r/32] (rows and r multiples of 32).
+hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, uint32_t *out, hipStream_t s);
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s);
 int gemm_tile_rows(GemmKind kind);
 hipError_t launch_colsum(const float *A, const float *B, int64_t M, int N, float *partial, hipStream_t s);

@@ -17,6 +17,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 // f16 bit patterns of +1 and -1.
 constexpr uint32_t F16_ONE = 0x3C00u;
@@ -112,20 +113,25 @@ hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // f16 MFMA contraction with fused staging (page: `cvt_col` feeding `mm`,
 // then `scale_acc` / `colsum_prod`):
-//   prod[m][n] = (sum_k f16(A[m][k] * colscale[k] * ascale) * B[n][k]) * oscale
-// B is an f16 sign plane [N][K]. Each workgroup computes a BM x BN tile with
-// WM x WN waves; each wave holds (BM/WM) x (BN/WN) f32 accumulators as
-// 32x32 MFMA tiles (v_mfma_f32_32x32x16_f16).
+//   prod[m][n] = (sum_k f16(A[m][k] * (colscale[k] * ascale)) * S[n][k]) * oscale
+// S is the +-1 plane [N][K], read as its bitmap (one u32 per row per K
+// step) and decoded to f16 while staging: the page's expanded f16 planes
+// are never materialised. ascale is a power of two, so folding it into
+// colscale rounds exactly like the page's (A * col) * scale except where an
+// f32 intermediate would overflow.
 //
-// Memory pipeline: the activation operand streams from HBM, so each thread
-// keeps P K-stages of global loads in flight in registers (a ring of P
-// register sets). A stage is converted to f16 and written to one of two LDS
-// buffers one iteration before it is multiplied.
+// Wave roles: a workgroup holds WM x WN "MMA" waves and as many "loader"
+// waves, so each SIMD runs one of each. Loader waves keep P K-stages of
+// global loads in flight in a statically indexed register ring, convert
+// the activation stage to f16 with its column scale and write both operand
+// tiles to one of two LDS buffers; MMA waves read fragments from the other
+// buffer and issue MFMAs (v_mfma_f32_32x32x16_f16, f32 accumulators). One
+// barrier per K step swaps the buffers, so the VALU staging of one wave and
+// the MFMAs of the other overlap on every SIMD.
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, each with its
-// own L2. The launch index is remapped so that consecutive tiles, which
-// share an activation row-block (the N tiles of one M tile), run on the
-// same XCD.
+// own L2. The launch index is remapped so that tiles sharing operands run
+// on the same XCD (see GM below).
 //
 // MFMA 32x32x16 operand layout: lane l supplies row (l % 32) of A and column
 // (l % 32) of B, each with the 8 consecutive k of group (l / 32). The
@@ -133,32 +139,84 @@ hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s) {
 // column l % 32.
 constexpr int NUM_XCD = 8;
 
-template <int BM, int BN, int BK, int WM, int WN, int P, bool OUT, bool OUT2, bool DOT, int GM>
-__global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
-    constexpr int NT = WM * WN * 64;
-    constexpr int LDK = BK + 8;  // halves per LDS row (pad: conflict-free 16-byte reads)
+// Signs of bits 0..15 of `w` (bit j = sign j; set = +1) as 16 f16 values:
+// lo = signs 0..7, hi = signs 8..15, two per dword (sign 2q in the low
+// half). Both 16-bit lanes of y hold the inverted bits; a packed shift moves
+// bit 2q (low lane) and bit 2q+1 (high lane) to the lanes' sign positions,
+// and the and-or keeps those sign bits over the pattern of +1.
+__device__ __forceinline__ uint32_t sign_dword(uint32_t y, int q, uint32_t sgnmask, uint32_t one16) {
+    const u16x2_t sh = {(uint16_t)(15 - 2 * q), (uint16_t)(14 - 2 * q)};
+    const u16x2_t t = __builtin_bit_cast(u16x2_t, y) << sh;
+    return (__builtin_bit_cast(uint32_t, t) & sgnmask) | one16;
+}
+// Signs of bits 0..UB-1 of `w` as UB f16 values in UB/8 16-byte groups.
+template <int UB>
+__device__ __forceinline__ void decode_signs(uint32_t w, uint32_t sgnmask, uint32_t one16, u32x4_t *d) {
+#pragma unroll
+    for (int h = 0; h < (UB + 15) / 16; ++h) {
+        const uint32_t y = (~(w >> (16 * h)) & 0xFFFFu) * 0x10001u;
+#pragma unroll
+        for (int q = 0; q < (UB < 16 ? UB / 2 : 8); ++q) d[2 * h + q / 4][q % 4] = sign_dword(y, q, sgnmask, one16);
+    }
+}
+
+// Bitmap transpose: out [r][rows/32] from bits [rows][r/32]; each thread
+// assembles one output word from 32 input words (rows 32*jw .. 32*jw+31,
+// rank k). Consecutive threads take consecutive ranks, so a wavefront reads
+// a few words per row (cache broadcasts).
+__global__ __launch_bounds__(256) void transpose_bits_kernel(const uint32_t *__restrict__ bits, int64_t rows,
+                                                             int64_t r, uint32_t *__restrict__ out) {
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rw = rows / 32, W = r / 32;
+    if (id >= r * rw) return;
+    const int64_t k = id % r, jw = id / r;
+    const uint32_t *src = bits + jw * 32 * W + k / 32;
+    const int sh = (int)(k % 32);
+    uint32_t word = 0;
+#pragma unroll 8
+    for (int b = 0; b < 32; ++b) word |= ((src[b * W] >> sh) & 1u) << b;
+    out[k * rw + jw] = word;
+}
+
+hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, uint32_t *out, hipStream_t s) {
+    const int64_t n = r * (rows / 32);
+    prof_begin(K_TRANSPOSE, s);
+    hipLaunchKernelGGL(transpose_bits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, bits, rows, r, out);
+    hipError_t e = hipGetLastError();
+    prof_end(s);
+    return e;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int LW, int P, bool OUT, bool OUT2, bool DOT, int GM>
+__global__ __launch_bounds__((1 + LW) * WM *WN * 64) void gemm_kernel(GemmArgs p) {
+    constexpr int NW = WM * WN;      // MMA waves; LW * NW loader waves
+    constexpr int NTR = LW * NW * 64;  // loader threads
+    constexpr int LDK = BK + 8;      // halves per LDS row (pad: conflict-free 16-byte reads)
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int A_CHUNKS = BM * BK / 4;  // float4 chunks of an A tile
-    constexpr int B_CHUNKS = BN * BK / 8;  // 16-byte chunks of a B tile
-    constexpr int A_PER = A_CHUNKS / NT, B_PER = B_CHUNKS / NT;
-    constexpr int AROW_STEP = NT / (BK / 4);
-    static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "tile/thread mismatch");
+    constexpr int A_CHUNKS = BM * BK / 4;   // float4 chunks of an A tile
+    constexpr int UB = BN * BK / NTR;       // signs of a B tile decoded per loader thread
+    constexpr int A_PER = A_CHUNKS / NTR;
+    constexpr int AROW_STEP = NTR / (BK / 4);
+    static_assert(BK == 32, "one bitmap word per plane row per K step");
+    static_assert(A_CHUNKS % NTR == 0 && (UB == 8 || UB == 16 || UB == 32), "tile/thread mismatch");
     static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "tile shape");
-    static_assert(NT % (BK / 4) == 0, "a thread keeps one column group of A");
+    static_assert(NTR % (BK / 4) == 0, "a loader thread keeps one column group of A");
     static_assert(P % 2 == 0, "LDS buffer index must be static in the unrolled loop");
-    // Epilogue staging: each wave writes 32 accumulator rows x TN columns of
-    // f32 to its own LDS region, then reads them back as row-contiguous
-    // float4. Row stride EPS = TN + 8 floats puts the two half-waves (rows r
-    // and r+4) on disjoint banks.
+    // Epilogue staging: each MMA wave writes 32 accumulator rows x TN
+    // columns of f32 to its own LDS region; the MMA wave and its first
+    // loader partner then read half the rows each as row-contiguous float4. Row
+    // stride EPS = TN + 8 floats puts the two half-waves (rows r and r+4) on
+    // disjoint banks.
     constexpr int EPS = TN + 8;
     constexpr int LANES_PER_ROW = TN / 4;
     constexpr int ROWS_PER_READ = 64 / LANES_PER_ROW;
+    constexpr int RPT = 16 / ROWS_PER_READ;  // row reads per strip per wave
     constexpr int LOOP_BYTES = 2 * (BM + BN) * LDK * 2;
-    constexpr int EPI_BYTES = (NT / 64) * 32 * EPS * 4;
-    constexpr int RED_BYTES = DOT ? WM * BN * 4 : 0;
+    constexpr int EPI_BYTES = NW * 32 * EPS * 4;
+    constexpr int RED_BYTES = DOT ? 2 * WM * BN * 4 : 0;
     constexpr int SMEM = LOOP_BYTES > EPI_BYTES + RED_BYTES ? LOOP_BYTES : EPI_BYTES + RED_BYTES;
-    static_assert(64 % LANES_PER_ROW == 0 && 32 % ROWS_PER_READ == 0, "epilogue read shape");
+    static_assert(64 % LANES_PER_ROW == 0 && 16 % ROWS_PER_READ == 0, "epilogue read shape");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     _Float16 *As0 = reinterpret_cast<_Float16 *>(smem);
@@ -167,8 +225,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
 #define BLR_BS(buf) (Bs0 + (buf) * (BN * LDK))
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: roles branch on scalars
+    const bool loader = wave >= NW;
+    const bool partner = loader && wave < 2 * NW;  // loader wave sharing an MMA wave's epilogue rows
+    const int rw = loader ? (wave - NW) % NW : wave;  // MMA wave index (a loader's partner)
+    const int wm = rw / WN, wn = rw % WN;
     const int N = p.N, K = p.K;
     const int ntn = N / BN;
     const int L = blockIdx.x, G = gridDim.x;
@@ -193,28 +255,34 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     const int nk = K / BK;  // a multiple of P (the launcher checks)
     const int64_t M = p.M;
 
-    // Per-thread operand pointers, fixed for the whole K loop. Rows past M
-    // read row M-1 instead: a row of the product depends on its own A row
-    // only, and those rows are never stored or summed.
-    const int c4 = tid % (BK / 4);
-    const int arow = tid / (BK / 4);
-    const float *abase[A_PER];
+    // Loader operand addressing: a uniform base advanced by the stage, plus
+    // a fixed 32-bit byte offset per thread (every operand is below 4 GiB,
+    // checked by the caller). Rows past M read row M-1 instead: a row of the
+    // product depends on its own A row only, and those rows are never stored
+    // or summed.
+    const int lt = loader ? tid - NW * 64 : 0;  // loader thread index
+    const int c4 = lt % (BK / 4);
+    const int arow = lt / (BK / 4);
+    uint32_t aoff[A_PER];
 #pragma unroll
     for (int v = 0; v < A_PER; ++v) {
         int64_t gm = m0 + arow + v * AROW_STEP;
         gm = gm < M ? gm : M - 1;
-        abase[v] = p.A + gm * p.lda + c4 * 4;
+        aoff[v] = (uint32_t)((gm * p.lda + c4 * 4) * 4);
     }
-    const float *cbase = p.colscale + c4 * 4;
-    const uint16_t *bbase[B_PER];
-    int bofs[B_PER];
-#pragma unroll
-    for (int v = 0; v < B_PER; ++v) {
-        const int idx = tid + v * NT;
-        const int row = idx / (BK / 8), c8 = idx % (BK / 8);
-        bbase[v] = p.B + (int64_t)(n0 + row) * K + c8 * 8;
-        bofs[v] = row * LDK + c8 * 8;
-    }
+    // B unit of this loader thread: plane row brow, signs bpart*UB ..
+    // bpart*UB + UB-1 of the K step's word
+    const int brow = lt / (32 / UB), bpart = lt % (32 / UB);
+    const uint32_t boff = (uint32_t)((int64_t)(n0 + brow) * (K / 32) * 4);
+    const int bofs = brow * LDK + bpart * UB;
+    const int bsh = bpart * UB;
+    // f16 sign patterns held in VGPRs so the decode's and-or is one VOP3
+    uint32_t sgnmask, one16;
+    asm volatile("v_mov_b32 %0, 0x80008000" : "=v"(sgnmask));
+    asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one16));
+    const unsigned char *Abytes = reinterpret_cast<const unsigned char *>(p.A);
+    const unsigned char *Bbytes = reinterpret_cast<const unsigned char *>(p.Bbits);
+    const unsigned char *Cbytes = reinterpret_cast<const unsigned char *>(p.colscale) + c4 * 16;
 
     f32x16_t acc[FM][FN];
 #pragma unroll
@@ -226,32 +294,36 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
 
     f32x4_t ar[P][A_PER];
     f32x4_t cr[P];
-    u32x4_t br[P][B_PER];
+    uint32_t br[P];
 
 #define BLR_GLOAD(q, kt)                                                                   \
     do {                                                                                   \
-        const int k0_ = (kt) * BK;                                                         \
+        const unsigned char *a_ = Abytes + (size_t)(kt) * (BK * 4);                        \
+        const unsigned char *b_ = Bbytes + (size_t)(kt) * 4;                               \
         _Pragma("unroll") for (int v = 0; v < A_PER; ++v) ar[q][v] =                       \
-            *reinterpret_cast<const f32x4_t *>(abase[v] + k0_);                            \
-        cr[q] = *reinterpret_cast<const f32x4_t *>(cbase + k0_);                           \
-        _Pragma("unroll") for (int v = 0; v < B_PER; ++v) br[q][v] =                       \
-            *reinterpret_cast<const u32x4_t *>(bbase[v] + k0_);                            \
+            *reinterpret_cast<const f32x4_t *>(a_ + aoff[v]);                              \
+        cr[q] = *reinterpret_cast<const f32x4_t *>(Cbytes + (size_t)(kt) * (BK * 4));      \
+        br[q] = *reinterpret_cast<const uint32_t *>(b_ + boff);                            \
     } while (0)
 
 #define BLR_SSTORE(q, buf)                                                                 \
     do {                                                                                   \
-        const f32x4_t cs_ = cr[q];                                                         \
-        const float s_ = p.ascale;                                                         \
+        const f32x4_t cs_ = cr[q] * p.ascale;                                              \
         _Pragma("unroll") for (int v = 0; v < A_PER; ++v) {                                \
             half4_t hv;                                                                    \
-            hv[0] = (_Float16)(ar[q][v].x * cs_.x * s_);                                   \
-            hv[1] = (_Float16)(ar[q][v].y * cs_.y * s_);                                   \
-            hv[2] = (_Float16)(ar[q][v].z * cs_.z * s_);                                   \
-            hv[3] = (_Float16)(ar[q][v].w * cs_.w * s_);                                   \
+            hv[0] = (_Float16)(ar[q][v].x * cs_.x);                                        \
+            hv[1] = (_Float16)(ar[q][v].y * cs_.y);                                        \
+            hv[2] = (_Float16)(ar[q][v].z * cs_.z);                                        \
+            hv[3] = (_Float16)(ar[q][v].w * cs_.w);                                        \
             *reinterpret_cast<half4_t *>(BLR_AS(buf) + (arow + v * AROW_STEP) * LDK + c4 * 4) = hv; \
         }                                                                                  \
-        _Pragma("unroll") for (int v = 0; v < B_PER; ++v)                                  \
-            *reinterpret_cast<u32x4_t *>(BLR_BS(buf) + bofs[v]) = br[q][v];                \
+        {                                                                                  \
+            u32x4_t d_[UB / 8];                                                            \
+            decode_signs<UB>(br[q] >> bsh, sgnmask, one16, d_);                            \
+            u32x4_t *bdst_ = reinterpret_cast<u32x4_t *>(                                  \
+                __builtin_assume_aligned(BLR_BS(buf) + bofs, 16));                         \
+            _Pragma("unroll") for (int e = 0; e < UB / 8; ++e) bdst_[e] = d_[e];           \
+        }                                                                                  \
     } while (0)
 
 #define BLR_COMPUTE(buf)                                                                   \
@@ -270,28 +342,40 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
         }                                                                                  \
     } while (0)
 
-    // prologue: stages 0..P-1 in flight, stage 0 staged into LDS buffer 0
+    // The two roles run separate loops with the same barriers: one per K
+    // step. In iteration kt the MMA waves multiply stage kt from LDS buffer
+    // kt&1 while the loaders issue stage kt+P into the register set stage kt
+    // used and stage kt+1 into the other buffer. The loader loop is
+    // unrolled by P so every register-set index is static; its loads are
+    // unconditional (stages past the end re-read the last stage and are
+    // never multiplied), so the compiler counts outstanding loads exactly and
+    // waits only for the stage it converts.
+    if (loader) {
 #pragma unroll
-    for (int q = 0; q < P; ++q) BLR_GLOAD(q, q);
-    BLR_SSTORE(0, 0);
-    __syncthreads();
-    // steady state, unrolled by P so every register-set index is static:
-    // iteration kt issues stage kt+P into the set stage kt used, multiplies
-    // stage kt, then stages kt+1 into the other LDS buffer. Loads and stores
-    // are unconditional (stages past the end re-read the last stage and are
-    // never multiplied), so the compiler can count outstanding loads exactly
-    // and wait only for the stage it converts.
-    for (int kt0 = 0; kt0 < nk; kt0 += P) {
+        for (int q = 0; q < P; ++q) BLR_GLOAD(q, q);
+        BLR_SSTORE(0, 0);
+        __syncthreads();
+        for (int kt0 = 0; kt0 < nk; kt0 += P) {
 #pragma unroll
-        for (int q = 0; q < P; ++q) {
-            const int kt = kt0 + q;
-            BLR_GLOAD(q, kt + P < nk ? kt + P : nk - 1);
-            BLR_COMPUTE(q & 1);
-            BLR_SSTORE((q + 1) % P, (q + 1) & 1);
-            __syncthreads();
-            // keep the next stages' conversions out of this iteration: hoisted
-            // above the barrier they would wait for loads just issued
-            __builtin_amdgcn_sched_barrier(0);
+            for (int q = 0; q < P; ++q) {
+                const int kt = kt0 + q;
+                BLR_GLOAD(q, kt + P < nk ? kt + P : nk - 1);
+                BLR_SSTORE((q + 1) % P, (q + 1) & 1);
+                __syncthreads();
+                // keep the next stages' conversions out of this iteration:
+                // hoisted above the barrier they would wait for loads just issued
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+        __syncthreads();
+        for (int kt0 = 0; kt0 < nk; kt0 += P) {
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                BLR_COMPUTE(q & 1);
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 #undef BLR_GLOAD
@@ -300,12 +384,14 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
 #undef BLR_AS
 #undef BLR_BS
 
-    // Epilogue, one 32-row strip of the wave tile at a time: stage the
-    // accumulators through LDS, then each lane handles float4 column groups
-    // of whole rows: products, tapes, scaled outputs and column partials.
-    constexpr int RPT = 32 / ROWS_PER_READ;  // row reads per strip per lane
-    float *stage = reinterpret_cast<float *>(smem) + wave * 32 * EPS;
-    const int lr0 = lane / LANES_PER_ROW;
+    // Epilogue, one 32-row strip of the MMA wave tiles at a time: the MMA
+    // waves stage their accumulators through LDS, then every wave handles
+    // float4 column groups of 16 whole rows (MMA wave: rows 0-15 of its
+    // strip, loader partner: rows 16-31): products, tapes, scaled outputs
+    // and column partials.
+    const float *stage = reinterpret_cast<const float *>(smem) + rw * 32 * EPS;
+    const bool epi = !loader || partner;  // waves that read back and store
+    const int lr0 = (loader ? 16 : 0) + lane / LANES_PER_ROW;
     const int lc = (lane % LANES_PER_ROW) * 4;
     const int gn = n0 + wn * TN + lc;
     const bool full = m0 + BM <= M;
@@ -315,7 +401,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     // lane's rows now (rows past M read row M-1 and are not used), so their
     // latencies overlap instead of following one another.
     f32x4_t pre[DOT ? FM : 1][DOT ? RPT : 1];
-    if (DOT) {
+    if (DOT && epi) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -329,7 +415,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         f32x4_t old[OUT2 ? RPT : 1];
-        if (OUT2 && p.out2acc) {
+        if (OUT2 && p.out2acc && epi) {
 #pragma unroll
             for (int it = 0; it < RPT; ++it) {
                 int64_t gm = m0 + wm * TM + i * 32 + it * ROWS_PER_READ + lr0;
@@ -337,14 +423,18 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
                 old[it] = *reinterpret_cast<const f32x4_t *>(p.out2 + gm * N + gn);
             }
         }
+        if (!loader) {
+            float *st = reinterpret_cast<float *>(smem) + rw * 32 * EPS;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                stage[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EPS + j * 32 + (lane & 31)] = acc[i][j][v];
+                for (int v = 0; v < 16; ++v)
+                    st[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EPS + j * 32 + (lane & 31)] = acc[i][j][v];
+        }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < RPT; ++it) {
+            if (!epi) break;
             const int lr = it * ROWS_PER_READ + lr0;
             const int64_t gm = m0 + wm * TM + i * 32 + lr;
             f32x4_t val = *reinterpret_cast<const f32x4_t *>(stage + lr * EPS + lc);
@@ -364,7 +454,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
     }
     if (DOT) {
         // lanes with the same columns (l mod LANES_PER_ROW) fold in a fixed
-        // butterfly, then the WM waves of a column strip add in wave order
+        // butterfly; then the 2*WM waves of a column strip (MMA waves first,
+        // then loaders, each in row order) add in that order
 #pragma unroll
         for (int off = LANES_PER_ROW; off < 64; off <<= 1) {
             dsum.x += __shfl_xor(dsum.x, off);
@@ -372,52 +463,44 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs p) {
             dsum.z += __shfl_xor(dsum.z, off);
             dsum.w += __shfl_xor(dsum.w, off);
         }
-        float *red = reinterpret_cast<float *>(smem + EPI_BYTES);  // [WM][BN]
-        if (lane < LANES_PER_ROW) *reinterpret_cast<f32x4_t *>(red + wm * BN + wn * TN + lc) = dsum;
+        float *red = reinterpret_cast<float *>(smem + EPI_BYTES);  // [2*WM][BN]
+        const int rrow = (loader ? WM : 0) + wm;
+        if (epi && lane < LANES_PER_ROW) *reinterpret_cast<f32x4_t *>(red + rrow * BN + wn * TN + lc) = dsum;
         __syncthreads();
-        for (int c = tid; c < BN; c += NT) {
-            float s = 0.0f;
+        for (int c = tid; c < BN; c += (1 + LW) * NW * 64) {
+            float sum = 0.0f;
 #pragma unroll
-            for (int w = 0; w < WM; ++w) s += red[w * BN + c];
-            p.dot_partial[(int64_t)mt * N + n0 + c] = s;
+            for (int w = 0; w < 2 * WM; ++w) sum += red[w * BN + c];
+            p.dot_partial[(int64_t)mt * N + n0 + c] = sum;
         }
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int P, bool OUT, bool OUT2, bool DOT, int GM>
+template <int BM, int BN, int BK, int WM, int WN, int LW, int P, bool OUT, bool OUT2, bool DOT, int GM>
 static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
     if (a.N % BN != 0 || a.K % (BK * P) != 0 || a.K / BK < P) return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)(a.N / BN) * ((a.M + BM - 1) / BM);
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WM, WN, P, OUT, OUT2, DOT, GM>), dim3((unsigned)tiles),
-                       dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WM, WN, LW, P, OUT, OUT2, DOT, GM>), dim3((unsigned)tiles),
+                       dim3((1 + LW) * WM * WN * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
 }
 
-// Tile shapes per kind (tuned at the headline size M=8192, d=4096, r=512).
-// F1/B1 (N = r, long K): 128x128 tiles; B1 runs 8 waves of 32x64. F2/B2
-// (N = d_out or d_in, K = r): 128x256 tiles of 8 waves, grouped tile order.
+// Tile shapes per kind: 128x128 tiles of 2x2 MMA waves (64x64 each) plus 4
+// loader waves; F2/B2/DH (N = d_out or d_in, K = r) walk groups of 8 M
+// tiles per N tile.
 int gemm_tile_rows(GemmKind) { return 128; }
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
-    const bool wide = a.N % 256 == 0;
     switch (kind) {
-        case GEMM_F1: return launch_gemm_t<128, 128, 32, 2, 2, 4, true, false, false, 1>(K_GEMM_F1, a, s);
-        case GEMM_F2:
-            if (wide) return launch_gemm_t<128, 256, 32, 2, 4, 4, true, true, false, 8>(K_GEMM_F2, a, s);
-            return launch_gemm_t<128, 128, 32, 2, 2, 4, true, true, false, 8>(K_GEMM_F2, a, s);
-        case GEMM_F2_NOTAPE:
-            if (wide) return launch_gemm_t<128, 256, 32, 2, 4, 4, false, true, false, 8>(K_GEMM_F2, a, s);
-            return launch_gemm_t<128, 128, 32, 2, 2, 4, false, true, false, 8>(K_GEMM_F2, a, s);
-        case GEMM_DH:
-            if (wide) return launch_gemm_t<128, 256, 32, 2, 4, 4, false, false, true, 8>(K_GEMM_DH, a, s);
-            return launch_gemm_t<128, 128, 32, 2, 2, 4, false, false, true, 8>(K_GEMM_DH, a, s);
-        case GEMM_B1: return launch_gemm_t<128, 128, 32, 4, 2, 4, true, false, true, 1>(K_GEMM_B1, a, s);
-        case GEMM_B2:
-            if (wide) return launch_gemm_t<128, 256, 32, 2, 4, 4, false, true, true, 8>(K_GEMM_B2, a, s);
-            return launch_gemm_t<128, 128, 32, 2, 2, 4, false, true, true, 8>(K_GEMM_B2, a, s);
+        case GEMM_F1: return launch_gemm_t<128, 128, 32, 2, 2, 1, 4, true, false, false, 1>(K_GEMM_F1, a, s);
+        case GEMM_F2: return launch_gemm_t<128, 128, 32, 2, 2, 1, 4, true, true, false, 8>(K_GEMM_F2, a, s);
+        case GEMM_F2_NOTAPE: return launch_gemm_t<128, 128, 32, 2, 2, 1, 4, false, true, false, 8>(K_GEMM_F2, a, s);
+        case GEMM_DH: return launch_gemm_t<128, 128, 32, 2, 2, 1, 4, false, false, true, 8>(K_GEMM_DH, a, s);
+        case GEMM_B1: return launch_gemm_t<128, 128, 32, 2, 2, 2, 4, true, false, true, 1>(K_GEMM_B1, a, s);
+        case GEMM_B2: return launch_gemm_t<128, 128, 32, 2, 2, 2, 4, false, true, true, 8>(K_GEMM_B2, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -508,6 +591,7 @@ hipError_t launch_finish(FinishJobs jobs, hipStream_t s) {
 const char *kernel_name(int id) {
     switch (id) {
         case K_EXPAND: return "expand_signs";
+        case K_TRANSPOSE: return "transpose_bits";
         case K_GEMM_F1: return "gemm_f1_xg_sv";
         case K_GEMM_F2: return "gemm_f2_al_sut";
         case K_GEMM_B1: return "gemm_b1_dyh_su";

@@ -54,12 +54,13 @@ def test_status_strings():
 
 def test_workspace_bytes():
     assert blr.blr_workspace_bytes(8192, 4096, 4096, 512) > 0
-    # planes (both orientations share one region per matrix) + db + partials
+    # transposed bitmap [r][max(d)/32] words + db [M][r] f32 + column partials
     n = blr.blr_workspace_bytes(128, 256, 256, 128)
-    assert n >= 2 * 128 * (256 + 256) + 4 * 128 * 128
+    assert n >= 4 * 128 * (256 // 32) + 4 * 128 * 128
     assert n % 256 == 0
     assert blr.blr_workspace_bytes(30000, 5120, 17408, 2048) >= 4 * 30000 * 2048
-    for bad in [(0, 256, 256, 128), (128, 200, 256, 128), (128, 256, 100, 128), (128, 256, 256, 64), (-1, 256, 256, 128)]:
+    for bad in [(0, 256, 256, 128), (128, 200, 256, 128), (128, 256, 100, 128), (128, 256, 256, 64), (-1, 256, 256, 128),
+                (1 << 21, 1 << 10, 1 << 10, 128)]:  # an operand of 8 GiB: beyond 32-bit byte offsets
         assert blr.blr_workspace_bytes(*bad) == 0
 
 
