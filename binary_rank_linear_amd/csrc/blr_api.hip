@@ -184,7 +184,7 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
     const void *f16a[] = {x, h, l, g, y, tape_a, tape_c ? tape_c : tape_a, workspace};
     for (const void *p : f16a)
         if (!aligned16(p)) return BLR_ERR_ALIGN;
-    if (!aligned4(bits_u) || !aligned4(bits_v)) return BLR_ERR_ALIGN;
+    if (!aligned16(bits_u) || !aligned16(bits_v)) return BLR_ERR_ALIGN;
     int st = current_device_ok();
     if (st != BLR_OK) return st;
 
@@ -237,7 +237,7 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     const void *f16a[] = {x, dy, h, l, g, tape_a, tape_c ? tape_c : tape_a, dh, dl, dg, dx, workspace};
     for (const void *p : f16a)
         if (!aligned16(p)) return BLR_ERR_ALIGN;
-    if (!aligned4(bits_u) || !aligned4(bits_v)) return BLR_ERR_ALIGN;
+    if (!aligned16(bits_u) || !aligned16(bits_v)) return BLR_ERR_ALIGN;
     int st = current_device_ok();
     if (st != BLR_OK) return st;
 

@@ -114,50 +114,70 @@ hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s) {
 // f16 MFMA contraction with fused staging (page: `cvt_col` feeding `mm`,
 // then `scale_acc` / `colsum_prod`):
 //   prod[m][n] = (sum_k f16(A[m][k] * (colscale[k] * ascale)) * S[n][k]) * oscale
-// S is the +-1 plane [N][K], read as its bitmap (one u32 per row per K
-// step) and decoded to f16 while staging: the page's expanded f16 planes
-// are never materialised. ascale is a power of two, so folding it into
-// colscale rounds exactly like the page's (A * col) * scale except where an
-// f32 intermediate would overflow.
+// S is the +-1 plane [N][K], read as its bitmap (one u32 per plane row per
+// K step of 32) and decoded to f16 in registers: the page's expanded f16
+// planes are never materialised. ascale is a power of two, so folding it
+// into colscale is exact except where an f32 intermediate would overflow.
 //
-// Wave roles: a workgroup holds WM x WN "MMA" waves and as many "loader"
-// waves, so each SIMD runs one of each. Loader waves keep P K-stages of
-// global loads in flight in a statically indexed register ring, convert
-// the activation stage to f16 with its column scale and write both operand
-// tiles to one of two LDS buffers; MMA waves read fragments from the other
-// buffer and issue MFMAs (v_mfma_f32_32x32x16_f16, f32 accumulators). One
-// barrier per K step swaps the buffers, so the VALU staging of one wave and
-// the MFMAs of the other overlap on every SIMD.
+// A workgroup of WM x WN waves computes a BM x BN tile; each wave owns a
+// TM x TN block of it. Per K step of 32:
+//  - activation: every thread keeps P stages of float4 loads in flight in a
+//    register ring (8 threads per row, so one wave load covers 8 whole
+//    128-byte rows). A stage is scaled and rounded to f16 with one fused
+//    multiply-and-convert per element and written to a 3-deep LDS ring two
+//    steps before it is used;
+//  - each wave reads the next step's A fragments from LDS while this
+//    step's MFMAs (v_mfma_f32_32x32x16_f16, f32 accumulators) run; one
+//    barrier per step;
+//  - sign operand: each wave decodes its own B fragments from the bitmap
+//    words (fetched 4 steps at a time, one group ahead) straight into
+//    registers; it never passes through LDS;
+//  - epilogue straight from the accumulators: for a fixed accumulator
+//    register the 64 lanes hold 2 rows x 32 consecutive columns, so every
+//    store instruction writes two whole 128-byte lines.
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, each with its
 // own L2. The launch index is remapped so that tiles sharing operands run
 // on the same XCD (see GM below).
 //
 // MFMA 32x32x16 operand layout: lane l supplies row (l % 32) of A and column
-// (l % 32) of B, each with the 8 consecutive k of group (l / 32). The
-// accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4,
-// column l % 32.
+// (l % 32) of B, each with the 8 consecutive k of group (l / 32) in each 16-k
+// block. The accumulator register v of lane l holds row
+// 8*(v/4) + 4*(l/32) + v%4, column l % 32.
 constexpr int NUM_XCD = 8;
 
-// Signs of bits 0..15 of `w` (bit j = sign j; set = +1) as 16 f16 values:
-// lo = signs 0..7, hi = signs 8..15, two per dword (sign 2q in the low
-// half). Both 16-bit lanes of y hold the inverted bits; a packed shift moves
-// bit 2q (low lane) and bit 2q+1 (high lane) to the lanes' sign positions,
-// and the and-or keeps those sign bits over the pattern of +1.
+// Two f16 lanes of one dword, each round(a * s) with a single rounding of
+// the exact product (round to nearest even; f16 subnormals kept, overflow
+// gives inf).
+__device__ __forceinline__ uint32_t f16x2_scaled(float a0, float s0, float a1, float s1) {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "=v"(r) : "v"(a0), "v"(s0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "+v"(r) : "v"(a1), "v"(s1));
+    return r;
+}
+
+// Signs 2q and 2q+1 of a byte as two f16 values of the NEGATED plane (set
+// bit -> -1, clear -> +1). Both 16-bit lanes of y hold the byte; a packed
+// shift moves bit 2q (low lane) and bit 2q+1 (high lane) to the lanes' sign
+// positions, and the and-or keeps those sign bits over the pattern of +1.
+// Decoding -S saves the inversion; the contraction's epilogue multiplies by
+// -oscale, which restores the sign exactly (round to nearest even is
+// symmetric, so every f32 partial sum is the exact negative).
 __device__ __forceinline__ uint32_t sign_dword(uint32_t y, int q, uint32_t sgnmask, uint32_t one16) {
     const u16x2_t sh = {(uint16_t)(15 - 2 * q), (uint16_t)(14 - 2 * q)};
     const u16x2_t t = __builtin_bit_cast(u16x2_t, y) << sh;
     return (__builtin_bit_cast(uint32_t, t) & sgnmask) | one16;
 }
-// Signs of bits 0..UB-1 of `w` as UB f16 values in UB/8 16-byte groups.
-template <int UB>
-__device__ __forceinline__ void decode_signs(uint32_t w, uint32_t sgnmask, uint32_t one16, u32x4_t *d) {
-#pragma unroll
-    for (int h = 0; h < (UB + 15) / 16; ++h) {
-        const uint32_t y = (~(w >> (16 * h)) & 0xFFFFu) * 0x10001u;
-#pragma unroll
-        for (int q = 0; q < (UB < 16 ? UB / 2 : 8); ++q) d[2 * h + q / 4][q % 4] = sign_dword(y, q, sgnmask, one16);
-    }
+// B fragment of -S: the 8 signs of byte `sel & 3` of w (sel replicates that
+// byte into all four bytes).
+__device__ __forceinline__ half8_t sign_frag(uint32_t w, uint32_t sel, uint32_t sgnmask, uint32_t one16) {
+    const uint32_t y = __builtin_amdgcn_perm(w, w, sel);
+    u32x4_t d;
+    d[0] = sign_dword(y, 0, sgnmask, one16);
+    d[1] = sign_dword(y, 1, sgnmask, one16);
+    d[2] = sign_dword(y, 2, sgnmask, one16);
+    d[3] = sign_dword(y, 3, sgnmask, one16);
+    return __builtin_bit_cast(half8_t, d);
 }
 
 // Bitmap transpose: out [r][rows/32] from bits [rows][r/32]; each thread
@@ -187,50 +207,28 @@ hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, 
     return e;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int LW, int P, bool OUT, bool OUT2, bool DOT, int GM>
-__global__ __launch_bounds__((1 + LW) * WM *WN * 64) void gemm_kernel(GemmArgs p) {
-    constexpr int NW = WM * WN;      // MMA waves; LW * NW loader waves
-    constexpr int NTR = LW * NW * 64;  // loader threads
-    constexpr int LDK = BK + 8;      // halves per LDS row (pad: conflict-free 16-byte reads)
+template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM>
+__global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int BK = 32;          // one bitmap word per plane row per step
+    constexpr int LDK = BK + 8;     // halves per LDS row (pad: conflict-free 16-byte reads)
+    constexpr int NS = 3;           // LDS ring depth
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int A_CHUNKS = BM * BK / 4;   // float4 chunks of an A tile
-    constexpr int UB = BN * BK / NTR;       // signs of a B tile decoded per loader thread
-    constexpr int A_PER = A_CHUNKS / NTR;
-    constexpr int AROW_STEP = NTR / (BK / 4);
-    static_assert(BK == 32, "one bitmap word per plane row per K step");
-    static_assert(A_CHUNKS % NTR == 0 && (UB == 8 || UB == 16 || UB == 32), "tile/thread mismatch");
-    static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "tile shape");
-    static_assert(NTR % (BK / 4) == 0, "a loader thread keeps one column group of A");
-    static_assert(P % 2 == 0, "LDS buffer index must be static in the unrolled loop");
-    // Epilogue staging: each MMA wave writes 32 accumulator rows x TN
-    // columns of f32 to its own LDS region; the MMA wave and its first
-    // loader partner then read half the rows each as row-contiguous float4. Row
-    // stride EPS = TN + 8 floats puts the two half-waves (rows r and r+4) on
-    // disjoint banks.
-    constexpr int EPS = TN + 8;
-    constexpr int LANES_PER_ROW = TN / 4;
-    constexpr int ROWS_PER_READ = 64 / LANES_PER_ROW;
-    constexpr int RPT = 16 / ROWS_PER_READ;  // row reads per strip per wave
-    constexpr int LOOP_BYTES = 2 * (BM + BN) * LDK * 2;
-    constexpr int EPI_BYTES = NW * 32 * EPS * 4;
-    constexpr int RED_BYTES = DOT ? 2 * WM * BN * 4 : 0;
-    constexpr int SMEM = LOOP_BYTES > EPI_BYTES + RED_BYTES ? LOOP_BYTES : EPI_BYTES + RED_BYTES;
-    static_assert(64 % LANES_PER_ROW == 0 && 16 % ROWS_PER_READ == 0, "epilogue read shape");
+    constexpr int TPR = BK / 4;     // threads per activation row, one float4 each
+    constexpr int RPP = NT / TPR;   // activation rows per pass
+    constexpr int PER = BM / RPP;   // float4 per thread per stage
+    static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % RPP == 0 && PER >= 1, "tile shape");
+    static_assert(4 % P == 0, "the register ring must divide the 4-step unroll");
+    static_assert(NT >= BN, "one thread per column for the column partials");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-    _Float16 *As0 = reinterpret_cast<_Float16 *>(smem);
-    _Float16 *Bs0 = reinterpret_cast<_Float16 *>(smem + 2 * BM * LDK * 2);
-#define BLR_AS(buf) (As0 + (buf) * (BM * LDK))
-#define BLR_BS(buf) (Bs0 + (buf) * (BN * LDK))
+    __shared__ __attribute__((aligned(16))) _Float16 As[NS * BM * LDK];
+    __shared__ float red[DOT ? WM * BN : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: roles branch on scalars
-    const bool loader = wave >= NW;
-    const bool partner = loader && wave < 2 * NW;  // loader wave sharing an MMA wave's epilogue rows
-    const int rw = loader ? (wave - NW) % NW : wave;  // MMA wave index (a loader's partner)
-    const int wm = rw / WN, wn = rw % WN;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
     const int N = p.N, K = p.K;
     const int ntn = N / BN;
     const int L = blockIdx.x, G = gridDim.x;
@@ -252,37 +250,38 @@ __global__ __launch_bounds__((1 + LW) * WM *WN * 64) void gemm_kernel(GemmArgs p
     }
     const int n0 = nt * BN;
     const int64_t m0 = (int64_t)mt * BM;
-    const int nk = K / BK;  // a multiple of P (the launcher checks)
+    const int nk = K / BK;  // a multiple of 4 (the launcher checks)
     const int64_t M = p.M;
 
-    // Loader operand addressing: a uniform base advanced by the stage, plus
-    // a fixed 32-bit byte offset per thread (every operand is below 4 GiB,
+    // Activation addressing: a uniform base advanced by the stage, plus a
+    // fixed 32-bit byte offset per thread (every operand is below 4 GiB,
     // checked by the caller). Rows past M read row M-1 instead: a row of the
     // product depends on its own A row only, and those rows are never stored
     // or summed.
-    const int lt = loader ? tid - NW * 64 : 0;  // loader thread index
-    const int c4 = lt % (BK / 4);
-    const int arow = lt / (BK / 4);
-    uint32_t aoff[A_PER];
+    const int c4 = tid % TPR, arow = tid / TPR;
+    uint32_t aoff[PER];
 #pragma unroll
-    for (int v = 0; v < A_PER; ++v) {
-        int64_t gm = m0 + arow + v * AROW_STEP;
+    for (int v = 0; v < PER; ++v) {
+        int64_t gm = m0 + arow + v * RPP;
         gm = gm < M ? gm : M - 1;
         aoff[v] = (uint32_t)((gm * p.lda + c4 * 4) * 4);
     }
-    // B unit of this loader thread: plane row brow, signs bpart*UB ..
-    // bpart*UB + UB-1 of the K step's word
-    const int brow = lt / (32 / UB), bpart = lt % (32 / UB);
-    const uint32_t boff = (uint32_t)((int64_t)(n0 + brow) * (K / 32) * 4);
-    const int bofs = brow * LDK + bpart * UB;
-    const int bsh = bpart * UB;
+    const unsigned char *Abytes = reinterpret_cast<const unsigned char *>(p.A);
+    const unsigned char *Cbytes = reinterpret_cast<const unsigned char *>(p.colscale) + c4 * 16;
+    const int wofs = arow * LDK + c4 * 4;                                   // LDS write, halves
+    const int rofs = (wm * TM + (lane & 31)) * LDK + (lane >> 5) * 8;      // fragment read, halves
+    // Bitmap words of this lane's plane rows (one per 32-column block)
+    const unsigned char *Bbytes = reinterpret_cast<const unsigned char *>(p.Bbits);
+    uint32_t boff[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) boff[j] = (uint32_t)((int64_t)(n0 + wn * TN + j * 32 + (lane & 31)) * (K / 32) * 4);
+    // v_perm selectors: byte (2s + lane group) of the word into every byte
+    const uint32_t grp = (uint32_t)(lane >> 5);
+    const uint32_t sel[2] = {grp * 0x01010101u, (2u + grp) * 0x01010101u};
     // f16 sign patterns held in VGPRs so the decode's and-or is one VOP3
     uint32_t sgnmask, one16;
     asm volatile("v_mov_b32 %0, 0x80008000" : "=v"(sgnmask));
     asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one16));
-    const unsigned char *Abytes = reinterpret_cast<const unsigned char *>(p.A);
-    const unsigned char *Bbytes = reinterpret_cast<const unsigned char *>(p.Bbits);
-    const unsigned char *Cbytes = reinterpret_cast<const unsigned char *>(p.colscale) + c4 * 16;
 
     f32x16_t acc[FM][FN];
 #pragma unroll
@@ -292,215 +291,220 @@ __global__ __launch_bounds__((1 + LW) * WM *WN * 64) void gemm_kernel(GemmArgs p
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    f32x4_t ar[P][A_PER];
+    f32x4_t ar[P][PER];
     f32x4_t cr[P];
-    uint32_t br[P];
+    u32x4_t bq[FN], bn[FN];  // bitmap words: this 4-step group, the next
+    half8_t fa[FM][2], fb[FN][2];
+    half8_t fa2[FM][2], fb2[FN][2];
 
 #define BLR_GLOAD(q, kt)                                                                   \
     do {                                                                                   \
-        const unsigned char *a_ = Abytes + (size_t)(kt) * (BK * 4);                        \
-        const unsigned char *b_ = Bbytes + (size_t)(kt) * 4;                               \
-        _Pragma("unroll") for (int v = 0; v < A_PER; ++v) ar[q][v] =                       \
+        const int k_ = (kt) < nk ? (kt) : nk - 1;                                          \
+        const unsigned char *a_ = Abytes + (size_t)k_ * (BK * 4);                          \
+        _Pragma("unroll") for (int v = 0; v < PER; ++v) ar[q][v] =                         \
             *reinterpret_cast<const f32x4_t *>(a_ + aoff[v]);                              \
-        cr[q] = *reinterpret_cast<const f32x4_t *>(Cbytes + (size_t)(kt) * (BK * 4));      \
-        br[q] = *reinterpret_cast<const uint32_t *>(b_ + boff);                            \
+        cr[q] = *reinterpret_cast<const f32x4_t *>(Cbytes + (size_t)k_ * (BK * 4));        \
+    } while (0)
+
+#define BLR_BLOAD(dst, grp4)                                                               \
+    do {                                                                                   \
+        const int g_ = (grp4) < nk / 4 ? (grp4) : nk / 4 - 1;                              \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) dst[j] =                            \
+            *reinterpret_cast<const u32x4_t *>(Bbytes + boff[j] + (size_t)g_ * 16);        \
     } while (0)
 
 #define BLR_SSTORE(q, buf)                                                                 \
     do {                                                                                   \
         const f32x4_t cs_ = cr[q] * p.ascale;                                              \
-        _Pragma("unroll") for (int v = 0; v < A_PER; ++v) {                                \
-            half4_t hv;                                                                    \
-            hv[0] = (_Float16)(ar[q][v].x * cs_.x);                                        \
-            hv[1] = (_Float16)(ar[q][v].y * cs_.y);                                        \
-            hv[2] = (_Float16)(ar[q][v].z * cs_.z);                                        \
-            hv[3] = (_Float16)(ar[q][v].w * cs_.w);                                        \
-            *reinterpret_cast<half4_t *>(BLR_AS(buf) + (arow + v * AROW_STEP) * LDK + c4 * 4) = hv; \
-        }                                                                                  \
-        {                                                                                  \
-            u32x4_t d_[UB / 8];                                                            \
-            decode_signs<UB>(br[q] >> bsh, sgnmask, one16, d_);                            \
-            u32x4_t *bdst_ = reinterpret_cast<u32x4_t *>(                                  \
-                __builtin_assume_aligned(BLR_BS(buf) + bofs, 16));                         \
-            _Pragma("unroll") for (int e = 0; e < UB / 8; ++e) bdst_[e] = d_[e];           \
+        _Float16 *dst_ = As + (buf) * (BM * LDK) + wofs;                                   \
+        _Pragma("unroll") for (int v = 0; v < PER; ++v) {                                  \
+            uint2 h_;                                                                      \
+            h_.x = f16x2_scaled(ar[q][v].x, cs_.x, ar[q][v].y, cs_.y);                     \
+            h_.y = f16x2_scaled(ar[q][v].z, cs_.z, ar[q][v].w, cs_.w);                     \
+            *reinterpret_cast<uint2 *>(dst_ + v * RPP * LDK) = h_;                          \
         }                                                                                  \
     } while (0)
 
-#define BLR_COMPUTE(buf)                                                                   \
+#define BLR_AFRAG(dst, buf)                                                                \
     do {                                                                                   \
-        _Pragma("unroll") for (int s = 0; s < BK / 16; ++s) {                              \
-            half8_t af[FM], bf[FN];                                                        \
-            _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] =                         \
-                *reinterpret_cast<const half8_t *>(                                        \
-                    BLR_AS(buf) + (wm * TM + i * 32 + (lane & 31)) * LDK + s * 16 + (lane >> 5) * 8); \
-            _Pragma("unroll") for (int j = 0; j < FN; ++j) bf[j] =                         \
-                *reinterpret_cast<const half8_t *>(                                        \
-                    BLR_BS(buf) + (wn * TN + j * 32 + (lane & 31)) * LDK + s * 16 + (lane >> 5) * 8); \
+        const _Float16 *src_ = As + (buf) * (BM * LDK) + rofs;                             \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                     \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s) dst[i][s] =                      \
+                *reinterpret_cast<const half8_t *>(src_ + i * 32 * LDK + s * 16);          \
+    } while (0)
+
+#define BLR_BFRAG(dst, words, u)                                                           \
+    do {                                                                                   \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                     \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s) dst[j][s] =                      \
+                sign_frag(words[j][u], sel[s], sgnmask, one16);                            \
+    } while (0)
+
+#define BLR_MMA(a_, b_)                                                                    \
+    do {                                                                                   \
+        _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
             _Pragma("unroll") for (int i = 0; i < FM; ++i)                                 \
                 _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] =                 \
-                    __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0); \
-        }                                                                                  \
+                    __builtin_amdgcn_mfma_f32_32x32x16_f16(a_[i][s], b_[j][s], acc[i][j], 0, 0, 0); \
     } while (0)
 
-    // The two roles run separate loops with the same barriers: one per K
-    // step. In iteration kt the MMA waves multiply stage kt from LDS buffer
-    // kt&1 while the loaders issue stage kt+P into the register set stage kt
-    // used and stage kt+1 into the other buffer. The loader loop is
-    // unrolled by P so every register-set index is static; its loads are
-    // unconditional (stages past the end re-read the last stage and are
-    // never multiplied), so the compiler counts outstanding loads exactly and
-    // waits only for the stage it converts.
-    if (loader) {
+    // Prologue: stages 0 and 1 into LDS buffers 0 and 1, the register ring
+    // refilled behind them, the bitmap words of groups 0 and 1, and the
+    // fragments of step 0.
 #pragma unroll
-        for (int q = 0; q < P; ++q) BLR_GLOAD(q, q);
-        BLR_SSTORE(0, 0);
-        __syncthreads();
-        for (int kt0 = 0; kt0 < nk; kt0 += P) {
+    for (int q = 0; q < P; ++q) BLR_GLOAD(q, q);
+    BLR_BLOAD(bq, 0);
+    BLR_BLOAD(bn, 1);
+    BLR_SSTORE(0, 0);
+    BLR_GLOAD(0, P);
+    BLR_SSTORE(1 % P, 1);
+    BLR_GLOAD(1 % P, P + 1);
+    __syncthreads();
+    BLR_AFRAG(fa, 0);
+    BLR_BFRAG(fb, bq, 0);
+    int b1 = 1, b2 = 2;  // LDS buffers of steps kt+1 and kt+2
+
+    // Iteration kt: fragments of step kt+1 are read and decoded while the
+    // MFMAs of step kt run, stage kt+2 goes to LDS and stage kt+2+P is
+    // loaded. Buffer kt+2 (mod 3) was last read in iteration kt-2. The
+    // loads are unconditional (stages and groups past the end re-read the
+    // last one and are never multiplied), so the compiler counts outstanding
+    // loads exactly and waits only for the stage it converts.
+    for (int kt0 = 0; kt0 < nk; kt0 += 4) {
 #pragma unroll
-            for (int q = 0; q < P; ++q) {
-                const int kt = kt0 + q;
-                BLR_GLOAD(q, kt + P < nk ? kt + P : nk - 1);
-                BLR_SSTORE((q + 1) % P, (q + 1) & 1);
-                __syncthreads();
-                // keep the next stages' conversions out of this iteration:
-                // hoisted above the barrier they would wait for loads just issued
-                __builtin_amdgcn_sched_barrier(0);
+        for (int u = 0; u < 4; ++u) {
+            const int kt = kt0 + u;
+            if (u % 2 == 0) {
+                BLR_AFRAG(fa2, b1);
+                BLR_BFRAG(fb2, bq, u + 1);
+                BLR_MMA(fa, fb);
+            } else {
+                BLR_AFRAG(fa, b1);
+                if (u < 3) {
+                    BLR_BFRAG(fb, bq, u + 1);
+                } else {
+                    BLR_BFRAG(fb, bn, 0);
+                }
+                BLR_MMA(fa2, fb2);
             }
-        }
-    } else {
-        __syncthreads();
-        for (int kt0 = 0; kt0 < nk; kt0 += P) {
+            if (u == 3) {
 #pragma unroll
-            for (int q = 0; q < P; ++q) {
-                BLR_COMPUTE(q & 1);
-                __syncthreads();
-                __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < FN; ++j) bq[j] = bn[j];
+                BLR_BLOAD(bn, kt0 / 4 + 2);
             }
+            BLR_SSTORE((u + 2) % P, b2);
+            BLR_GLOAD((u + 2) % P, kt + 2 + P);
+            __syncthreads();
+            // keep later steps' work out of this one: hoisted above the
+            // barrier it would wait for loads issued just before
+            __builtin_amdgcn_sched_barrier(0);
+            b1 = b2;
+            b2 = b2 == NS - 1 ? 0 : b2 + 1;
         }
     }
 #undef BLR_GLOAD
+#undef BLR_BLOAD
 #undef BLR_SSTORE
-#undef BLR_COMPUTE
-#undef BLR_AS
-#undef BLR_BS
+#undef BLR_AFRAG
+#undef BLR_BFRAG
+#undef BLR_MMA
 
-    // Epilogue, one 32-row strip of the MMA wave tiles at a time: the MMA
-    // waves stage their accumulators through LDS, then every wave handles
-    // float4 column groups of 16 whole rows (MMA wave: rows 0-15 of its
-    // strip, loader partner: rows 16-31): products, tapes, scaled outputs
-    // and column partials.
-    const float *stage = reinterpret_cast<const float *>(smem) + rw * 32 * EPS;
-    const bool epi = !loader || partner;  // waves that read back and store
-    const int lr0 = (loader ? 16 : 0) + lane / LANES_PER_ROW;
-    const int lc = (lane % LANES_PER_ROW) * 4;
-    const int gn = n0 + wn * TN + lc;
+    // Epilogue from the accumulators: products, tapes, scaled outputs and
+    // column partials. Rows past M are neither stored nor summed (their
+    // loads read row M-1).
+    const float osc = -p.oscale;  // the fragments hold -S
+    const int64_t rb = m0 + wm * TM + 4 * (lane >> 5);
+    const int cb = n0 + wn * TN + (lane & 31);
     const bool full = m0 + BM <= M;
-    f32x4_t c2 = {0.f, 0.f, 0.f, 0.f};
-    if (OUT2) c2 = *reinterpret_cast<const f32x4_t *>(p.out2col + gn);
-    // The column-sum operand streams from HBM once: issue every load of this
-    // lane's rows now (rows past M read row M-1 and are not used), so their
-    // latencies overlap instead of following one another.
-    f32x4_t pre[DOT ? FM : 1][DOT ? RPT : 1];
-    if (DOT && epi) {
+    float c2[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) c2[j] = OUT2 ? p.out2col[cb + j * 32] : 0.0f;
+    float dsum[FN];
 #pragma unroll
-            for (int it = 0; it < RPT; ++it) {
-                int64_t gm = m0 + wm * TM + i * 32 + it * ROWS_PER_READ + lr0;
-                gm = gm < M ? gm : M - 1;
-                pre[i][it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p.dot_other + gm * N + gn));
-            }
-    }
-    f32x4_t dsum = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) dsum[j] = 0.0f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        f32x4_t old[OUT2 ? RPT : 1];
-        if (OUT2 && p.out2acc && epi) {
+        // the operands this block reads from HBM, all issued before use
+        float oth[DOT ? FN : 1][DOT ? 16 : 1], old[OUT2 ? FN : 1][OUT2 ? 16 : 1];
 #pragma unroll
-            for (int it = 0; it < RPT; ++it) {
-                int64_t gm = m0 + wm * TM + i * 32 + it * ROWS_PER_READ + lr0;
-                gm = gm < M ? gm : M - 1;
-                old[it] = *reinterpret_cast<const f32x4_t *>(p.out2 + gm * N + gn);
+        for (int v = 0; v < 16; ++v) {
+            int64_t gm = rb + i * 32 + 8 * (v >> 2) + (v & 3);
+            gm = gm < M ? gm : M - 1;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if (DOT) oth[j][v] = __builtin_nontemporal_load(p.dot_other + gm * N + cb + j * 32);
+                if (OUT2) old[j][v] = p.out2acc ? p.out2[gm * N + cb + j * 32] : 0.0f;
             }
         }
-        if (!loader) {
-            float *st = reinterpret_cast<float *>(smem) + rw * 32 * EPS;
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    st[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EPS + j * 32 + (lane & 31)] = acc[i][j][v];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < RPT; ++it) {
-            if (!epi) break;
-            const int lr = it * ROWS_PER_READ + lr0;
-            const int64_t gm = m0 + wm * TM + i * 32 + lr;
-            f32x4_t val = *reinterpret_cast<const f32x4_t *>(stage + lr * EPS + lc);
-            val *= p.oscale;
+        for (int v = 0; v < 16; ++v) {
+            const int64_t gm = rb + i * 32 + 8 * (v >> 2) + (v & 3);
             if (full || gm < M) {
-                const int64_t o = gm * N + gn;
-                if (OUT) *reinterpret_cast<f32x4_t *>(p.out + o) = val;
-                if (OUT2) {
-                    f32x4_t y = val * c2;
-                    if (p.out2acc) y = old[it] + y;
-                    *reinterpret_cast<f32x4_t *>(p.out2 + o) = y;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const float val = acc[i][j][v] * osc;
+                    const int64_t o = gm * N + cb + j * 32;
+                    if (OUT) p.out[o] = val;
+                    if (OUT2) p.out2[o] = old[j][v] + val * c2[j];
+                    if (DOT) dsum[j] += val * oth[j][v];
                 }
-                if (DOT) dsum += val * pre[i][it];
             }
         }
-        __syncthreads();
     }
     if (DOT) {
-        // lanes with the same columns (l mod LANES_PER_ROW) fold in a fixed
-        // butterfly; then the 2*WM waves of a column strip (MMA waves first,
-        // then loaders, each in row order) add in that order
+        // lanes l and l+32 hold the same columns; then the WM waves of a
+        // column strip add in row order
 #pragma unroll
-        for (int off = LANES_PER_ROW; off < 64; off <<= 1) {
-            dsum.x += __shfl_xor(dsum.x, off);
-            dsum.y += __shfl_xor(dsum.y, off);
-            dsum.z += __shfl_xor(dsum.z, off);
-            dsum.w += __shfl_xor(dsum.w, off);
+        for (int j = 0; j < FN; ++j) {
+            dsum[j] += __shfl_xor(dsum[j], 32);
+            if (lane < 32) red[wm * BN + wn * TN + j * 32 + lane] = dsum[j];
         }
-        float *red = reinterpret_cast<float *>(smem + EPI_BYTES);  // [2*WM][BN]
-        const int rrow = (loader ? WM : 0) + wm;
-        if (epi && lane < LANES_PER_ROW) *reinterpret_cast<f32x4_t *>(red + rrow * BN + wn * TN + lc) = dsum;
         __syncthreads();
-        for (int c = tid; c < BN; c += (1 + LW) * NW * 64) {
+        if (tid < BN) {
             float sum = 0.0f;
 #pragma unroll
-            for (int w = 0; w < 2 * WM; ++w) sum += red[w * BN + c];
-            p.dot_partial[(int64_t)mt * N + n0 + c] = sum;
+            for (int w = 0; w < WM; ++w) sum += red[w * BN + tid];
+            p.dot_partial[(int64_t)mt * N + n0 + tid] = sum;
         }
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int LW, int P, bool OUT, bool OUT2, bool DOT, int GM>
+template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM>
 static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
-    if (a.N % BN != 0 || a.K % (BK * P) != 0 || a.K / BK < P) return hipErrorInvalidValue;
+    if (a.N % BN != 0 || a.K % 128 != 0 || a.K < 128) return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)(a.N / BN) * ((a.M + BM - 1) / BM);
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WM, WN, LW, P, OUT, OUT2, DOT, GM>), dim3((unsigned)tiles),
-                       dim3((1 + LW) * WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM>), dim3((unsigned)tiles),
+                       dim3(WM * WN * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
 }
 
-// Tile shapes per kind: 128x128 tiles of 2x2 MMA waves (64x64 each) plus 4
-// loader waves; F2/B2/DH (N = d_out or d_in, K = r) walk groups of 8 M
-// tiles per N tile.
-int gemm_tile_rows(GemmKind) { return 128; }
+// Tile shapes per kind (measured at M=8192, d=4096, r=512): F1 with 64x128
+// tiles of 1x4 waves (64x32 each, twice as many workgroups as CUs); F2 and
+// B2 (N = d_out or d_in, K = r, an f32 [M][N] output) with 128x256 tiles of
+// 2x4 waves when N is a multiple of 256, else 128x128 tiles of 2x2 waves; DH
+// with 128x128 tiles of 2x2 waves; B1 with 128x128 tiles of 2x4 waves. The
+// kinds with N = d_out or d_in walk groups of 8 M tiles per N tile. Every
+// kind with column partials uses 128-row tiles.
+int gemm_tile_rows(GemmKind kind) { return kind == GEMM_F1 ? 64 : 128; }
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
+    const bool wide = a.N % 256 == 0;
     switch (kind) {
-        case GEMM_F1: return launch_gemm_t<128, 128, 32, 2, 2, 1, 4, true, false, false, 1>(K_GEMM_F1, a, s);
-        case GEMM_F2: return launch_gemm_t<128, 128, 32, 2, 2, 1, 4, true, true, false, 8>(K_GEMM_F2, a, s);
-        case GEMM_F2_NOTAPE: return launch_gemm_t<128, 128, 32, 2, 2, 1, 4, false, true, false, 8>(K_GEMM_F2, a, s);
-        case GEMM_DH: return launch_gemm_t<128, 128, 32, 2, 2, 1, 4, false, false, true, 8>(K_GEMM_DH, a, s);
-        case GEMM_B1: return launch_gemm_t<128, 128, 32, 2, 2, 2, 4, true, false, true, 1>(K_GEMM_B1, a, s);
-        case GEMM_B2: return launch_gemm_t<128, 128, 32, 2, 2, 2, 4, false, true, true, 8>(K_GEMM_B2, a, s);
+        case GEMM_F1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1>(K_GEMM_F1, a, s);
+        case GEMM_F2:
+            return wide ? launch_gemm_t<128, 256, 2, 4, 2, 2, true, true, false, 8>(K_GEMM_F2, a, s)
+                        : launch_gemm_t<128, 128, 2, 2, 2, 2, true, true, false, 8>(K_GEMM_F2, a, s);
+        case GEMM_F2_NOTAPE:
+            return wide ? launch_gemm_t<128, 256, 2, 4, 2, 2, false, true, false, 8>(K_GEMM_F2, a, s)
+                        : launch_gemm_t<128, 128, 2, 2, 2, 2, false, true, false, 8>(K_GEMM_F2, a, s);
+        case GEMM_DH: return launch_gemm_t<128, 128, 2, 2, 2, 2, false, false, true, 8>(K_GEMM_DH, a, s);
+        case GEMM_B1: return launch_gemm_t<128, 128, 2, 4, 2, 2, true, false, true, 1>(K_GEMM_B1, a, s);
+        case GEMM_B2:
+            return wide ? launch_gemm_t<128, 256, 2, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s)
+                        : launch_gemm_t<128, 128, 2, 2, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s);
     }
     return hipErrorInvalidValue;
 }

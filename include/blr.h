@@ -95,8 +95,9 @@ int blr_expand_signs(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl
  *     recomputes it with the same contraction (bit-identical c): 2*M*r*d_out
  *     more MFMA flops instead of 8*M*d_out bytes of HBM traffic.
  *   The tapes must come from a forward on the same x and parameters.
- * Planes are expanded into the workspace on every call (the page re-expands
- * per layer call). Float pointers must be 16-byte aligned.
+ * The sign planes are decoded from the bitmaps on every call (the page
+ * re-expands its planes per layer call). Float and bitmap pointers must be
+ * 16-byte aligned.
  */
 int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
                 const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y, int accumulate_y,
@@ -113,7 +114,7 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
  *   dh [d_out], dl [r], dg [d_in]: always accumulate (+=); zero them first
  *     for a plain gradient.
  *   dx [M][d_in]: accumulate_dx = 0 writes dx = g.dx', 1 adds.
- * Float pointers must be 16-byte aligned.
+ * Float and bitmap pointers must be 16-byte aligned.
  */
 int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
                  const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,

@@ -153,6 +153,12 @@ def test_rejects_misaligned(ptrs):
     p = dict(ptrs)
     p["dx"] = f(offset=8)
     assert bwd(lib, 128, 256, 256, 128, p) == E_ALIGN
+    # bitmaps are read as 16-byte groups of 4 words
+    for k in ["bu", "bv"]:
+        p = dict(ptrs)
+        p[k] = f(offset=4)
+        assert fwd(lib, 128, 256, 256, 128, p) == E_ALIGN, k
+        assert bwd(lib, 128, 256, 256, 128, p) == E_ALIGN, k
 
 
 def test_expand_rejects_bad_arguments(ptrs):
