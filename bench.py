@@ -34,25 +34,30 @@ RIDGE = PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
 
 def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[float, float]:
     """Algorithmic (bytes, flops) of one launch of a kernel: the bytes each
-    kernel must move between HBM and the chip at minimum (f32 activations,
-    f16 sign planes read once) and the MFMA flops of its contraction."""
+    kernel must move between HBM and the chip at minimum (f32 activations in
+    and out once, the 1-bit sign bitmap once, the per-column scales) and the
+    MFMA flops of its contraction."""
     M, di, do, r = w.M, w.d_in, w.d_out, w.r
-    f32, f16 = 4, 2
-    if name == "gemm_f1_xg_sv":      # read x, write tape a, plane [r][d_in]
-        return M * (di + r) * f32 + r * di * f16 + di * f32, 2.0 * M * r * di
-    if name == "gemm_f2_al_sut":     # read a, write y (and the c tape), plane [d_out][r]
-        return M * (r + (2 if keep_c else 1) * do) * f32 + do * r * f16 + (r + do) * f32, 2.0 * M * do * r
-    if name == "gemm_dh_recompute_c":  # read a and dy, plane [d_out][r]; dh partials are negligible
-        return M * (r + do) * f32 + do * r * f16 + r * f32, 2.0 * M * do * r
-    if name == "gemm_b1_dyh_su":     # read dy and a, write db, plane [r][d_out]
-        return M * (do + 2 * r) * f32 + r * do * f16 + do * f32, 2.0 * M * r * do
-    if name == "gemm_b2_dbl_svt":    # read db and x, write dx, plane [d_in][r]
-        return M * (r + 2 * di) * f32 + di * r * f16 + (r + di) * f32, 2.0 * M * di * r
+    f32 = 4
+    if name == "gemm_f1_xg_sv":      # read x, write tape a; bitmap of S_V
+        return M * (di + r) * f32 + r * di / 8 + di * f32, 2.0 * M * r * di
+    if name == "gemm_f2_al_sut":     # read a, write y (and the c tape); bitmap of S_U
+        return M * (r + (2 if keep_c else 1) * do) * f32 + do * r / 8 + (r + do) * f32, 2.0 * M * do * r
+    if name == "gemm_dh_recompute_c":  # read a and dy; dh partials are negligible
+        return M * (r + do) * f32 + do * r / 8 + r * f32, 2.0 * M * do * r
+    if name == "gemm_b1_dyh_su":     # read dy and a, write db
+        return M * (do + 2 * r) * f32 + r * do / 8 + do * f32, 2.0 * M * r * do
+    if name == "gemm_b2_dbl_svt":    # read db and x, write dx
+        return M * (r + 2 * di) * f32 + di * r / 8 + (r + di) * f32, 2.0 * M * di * r
     if name == "colsum_dy_c":        # read dy and c
         return 2.0 * M * do * f32, 2.0 * M * do
+    if name == "transpose_bits":     # one bitmap in, its transpose out (average of U and V)
+        return 2 * r * (di + do) / 2 / 8, 0.0
+    if name == "colsum_finish":      # read the column partials of dh, dl, dg
+        return -(-M // 128) * (do + r + di) * f32, 0.0
     if name == "expand_signs":       # per launch: one bitmap in, one f16 plane out (average of U and V)
         rows = (di + do) / 2
-        return rows * (r / 8 + r * f16), 0.0
+        return rows * (r / 8 + r * 2), 0.0
     return 0.0, 0.0
 
 
