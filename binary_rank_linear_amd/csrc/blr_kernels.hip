@@ -156,6 +156,33 @@ __device__ __forceinline__ uint32_t f16x2_scaled(float a0, float s0, float a1, f
     return r;
 }
 
+// Raw buffer access (offset = per-lane VGPR byte offset + uniform byte
+// offset, computed by the address unit). The range is the operand's size.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0,
+                                             (int)(uint32_t)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull),
+                                             0x00020000);
+}
+__device__ __forceinline__ f32x4_t load_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x4_t load_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+// streaming (non-temporal) variants: the data is not re-read soon
+__device__ __forceinline__ float load_f32_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 2));
+}
+__device__ __forceinline__ void store_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void store_f32_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 2);
+}
+
 // Signs 2q and 2q+1 of a byte as two f16 values of the NEGATED plane (set
 // bit -> -1, clear -> +1). Both 16-bit lanes of y hold the byte; a packed
 // shift moves bit 2q (low lane) and bit 2q+1 (high lane) to the lanes' sign
@@ -266,12 +293,16 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
         gm = gm < M ? gm : M - 1;
         aoff[v] = (uint32_t)((gm * p.lda + c4 * 4) * 4);
     }
-    const unsigned char *Abytes = reinterpret_cast<const unsigned char *>(p.A);
-    const unsigned char *Cbytes = reinterpret_cast<const unsigned char *>(p.colscale) + c4 * 16;
+    // Buffer resources: every operand below 4 GiB (checked by the caller);
+    // the loads take a 32-bit per-lane offset plus a uniform offset, so no
+    // VALU address arithmetic is needed.
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)M * p.lda * 4);
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.colscale, (uint64_t)K * 4);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.Bbits, (uint64_t)N * K / 8);
+    const uint32_t coff = (uint32_t)c4 * 16;
     const int wofs = arow * LDK + c4 * 4;                                   // LDS write, halves
     const int rofs = (wm * TM + (lane & 31)) * LDK + (lane >> 5) * 8;      // fragment read, halves
     // Bitmap words of this lane's plane rows (one per 32-column block)
-    const unsigned char *Bbytes = reinterpret_cast<const unsigned char *>(p.Bbits);
     uint32_t boff[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) boff[j] = (uint32_t)((int64_t)(n0 + wn * TN + j * 32 + (lane & 31)) * (K / 32) * 4);
@@ -300,17 +331,16 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
 #define BLR_GLOAD(q, kt)                                                                   \
     do {                                                                                   \
         const int k_ = (kt) < nk ? (kt) : nk - 1;                                          \
-        const unsigned char *a_ = Abytes + (size_t)k_ * (BK * 4);                          \
         _Pragma("unroll") for (int v = 0; v < PER; ++v) ar[q][v] =                         \
-            *reinterpret_cast<const f32x4_t *>(a_ + aoff[v]);                              \
-        cr[q] = *reinterpret_cast<const f32x4_t *>(Cbytes + (size_t)k_ * (BK * 4));        \
+            load_f32x4(rA, aoff[v], (uint32_t)k_ * (BK * 4));                              \
+        cr[q] = load_f32x4(rC, coff, (uint32_t)k_ * (BK * 4));                             \
     } while (0)
 
 #define BLR_BLOAD(dst, grp4)                                                               \
     do {                                                                                   \
         const int g_ = (grp4) < nk / 4 ? (grp4) : nk / 4 - 1;                              \
         _Pragma("unroll") for (int j = 0; j < FN; ++j) dst[j] =                            \
-            *reinterpret_cast<const u32x4_t *>(Bbytes + boff[j] + (size_t)g_ * 16);        \
+            load_u32x4(rB, boff[j], (uint32_t)g_ * 16);                                    \
     } while (0)
 
 #define BLR_SSTORE(q, buf)                                                                 \
@@ -410,47 +440,56 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
 #undef BLR_MMA
 
     // Epilogue from the accumulators: products, tapes, scaled outputs and
-    // column partials. Rows past M are neither stored nor summed (their
-    // loads read row M-1).
+    // column partials. Element (i, v, j) of a lane sits at row
+    // rl + i*32 + 8*(v/4) + v%4 and column cb + j*32; the lane part of the
+    // byte offset is a VGPR, the rest a uniform offset. Rows past M are
+    // neither loaded, stored nor summed (only a tile that ends past M checks).
     const float osc = -p.oscale;  // the fragments hold -S
-    const int64_t rb = m0 + wm * TM + 4 * (lane >> 5);
+    const int64_t rl = m0 + wm * TM + 4 * (lane >> 5);
     const int cb = n0 + wn * TN + (lane & 31);
+    const uint32_t loff = (uint32_t)((rl * N + cb) * 4);
     const bool full = m0 + BM <= M;
+    const uint64_t obytes = (uint64_t)M * N * 4;
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(p.out, OUT ? obytes : 0);
+    const __amdgpu_buffer_rsrc_t rO2 = make_rsrc(p.out2, OUT2 ? obytes : 0);
+    const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.dot_other, DOT ? obytes : 0);
     float c2[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) c2[j] = OUT2 ? p.out2col[cb + j * 32] : 0.0f;
     float dsum[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) dsum[j] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        // the operands this block reads from HBM, all issued before use
-        float oth[DOT ? FN : 1][DOT ? 16 : 1], old[OUT2 ? FN : 1][OUT2 ? 16 : 1];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            int64_t gm = rb + i * 32 + 8 * (v >> 2) + (v & 3);
-            gm = gm < M ? gm : M - 1;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                if (DOT) oth[j][v] = __builtin_nontemporal_load(p.dot_other + gm * N + cb + j * 32);
-                if (OUT2) old[j][v] = p.out2acc ? p.out2[gm * N + cb + j * 32] : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t gm = rb + i * 32 + 8 * (v >> 2) + (v & 3);
-            if (full || gm < M) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const float val = acc[i][j][v] * osc;
-                    const int64_t o = gm * N + cb + j * 32;
-                    if (OUT) p.out[o] = val;
-                    if (OUT2) p.out2[o] = old[j][v] + val * c2[j];
-                    if (DOT) dsum[j] += val * oth[j][v];
-                }
-            }
-        }
+#define BLR_UOFF(i, v, j) ((uint32_t)(((i) * 32 + 8 * ((v) >> 2) + ((v) & 3)) * N + (j) * 32) * 4u)
+#define BLR_EPI_BLOCK(GUARD)                                                               \
+    do {                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                   \
+            float oth[DOT ? FN : 1][DOT ? 16 : 1], old[OUT2 ? FN : 1][OUT2 ? 16 : 1];      \
+            _Pragma("unroll") for (int v = 0; v < 16; ++v) {                               \
+                const bool in_ = !(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M;     \
+                _Pragma("unroll") for (int j = 0; j < FN; ++j) {                           \
+                    if (DOT) oth[j][v] = in_ ? load_f32_nt(rD, loff, BLR_UOFF(i, v, j)) : 0.0f; \
+                    if (OUT2) old[j][v] = (p.out2acc && in_) ? load_f32(rO2, loff, BLR_UOFF(i, v, j)) : 0.0f; \
+                }                                                                          \
+            }                                                                              \
+            _Pragma("unroll") for (int v = 0; v < 16; ++v) {                               \
+                if (!(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M) {                \
+                    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                       \
+                        const float val = acc[i][j][v] * osc;                              \
+                        if (OUT) store_f32(rO, loff, BLR_UOFF(i, v, j), val);              \
+                        if (OUT2) store_f32_nt(rO2, loff, BLR_UOFF(i, v, j), old[j][v] + val * c2[j]); \
+                        if (DOT) dsum[j] += val * oth[j][v];                               \
+                    }                                                                      \
+                }                                                                          \
+            }                                                                              \
+        }                                                                                  \
+    } while (0)
+    if (full) {
+        BLR_EPI_BLOCK(false);
+    } else {
+        BLR_EPI_BLOCK(true);
     }
+#undef BLR_EPI_BLOCK
+#undef BLR_UOFF
     if (DOT) {
         // lanes l and l+32 hold the same columns; then the WM waves of a
         // column strip add in row order
