@@ -146,14 +146,17 @@ hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s) {
 // 8*(v/4) + 4*(l/32) + v%4, column l % 32.
 constexpr int NUM_XCD = 8;
 
-// Two f16 lanes of one dword, each round(a * s) with a single rounding of
-// the exact product (round to nearest even; f16 subnormals kept, overflow
-// gives inf).
+// Two f16 lanes of one dword: f16(a0 * s0), f16(a1 * s1), each product
+// rounded to f32 and then to f16 (round to nearest even; f16 subnormals
+// kept, overflow gives inf). On gfx950 this is two multiplies and one
+// packed conversion, all of which issue while an MFMA runs (a fused
+// multiply-and-convert to f16 does not).
 __device__ __forceinline__ uint32_t f16x2_scaled(float a0, float s0, float a1, float s1) {
-    uint32_t r;
-    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "=v"(r) : "v"(a0), "v"(s0));
-    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "+v"(r) : "v"(a1), "v"(s1));
-    return r;
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    half2_t h;
+    h[0] = (_Float16)(a0 * s0);
+    h[1] = (_Float16)(a1 * s1);
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // Raw buffer access (offset = per-lane VGPR byte offset + uniform byte
@@ -207,28 +210,37 @@ __device__ __forceinline__ half8_t sign_frag(uint32_t w, uint32_t sel, uint32_t 
     return __builtin_bit_cast(half8_t, d);
 }
 
-// Bitmap transpose: out [r][rows/32] from bits [rows][r/32]; each thread
-// assembles one output word from 32 input words (rows 32*jw .. 32*jw+31,
-// rank k). Consecutive threads take consecutive ranks, so a wavefront reads
-// a few words per row (cache broadcasts).
+// Bitmap transpose: out [r][rows/32] from bits [rows][r/32]. A wavefront
+// takes 64 rows x one word column (32 ranks): each lane loads its row's word,
+// then one wave-wide ballot per bit position gives, for rank 32w+b, the
+// 64-bit mask of those rows; lane b keeps it and writes the two output words.
 __global__ __launch_bounds__(256) void transpose_bits_kernel(const uint32_t *__restrict__ bits, int64_t rows,
                                                              int64_t r, uint32_t *__restrict__ out) {
-    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t rw = rows / 32, W = r / 32;
-    if (id >= r * rw) return;
-    const int64_t k = id % r, jw = id / r;
-    const uint32_t *src = bits + jw * 32 * W + k / 32;
-    const int sh = (int)(k % 32);
-    uint32_t word = 0;
-#pragma unroll 8
-    for (int b = 0; b < 32; ++b) word |= ((src[b * W] >> sh) & 1u) << b;
-    out[k * rw + jw] = word;
+    const int64_t W = r / 32, rw = rows / 32;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // one wavefront per (row block, word)
+    const int lane = threadIdx.x & 63;
+    const int64_t nrb = (rows + 63) / 64;
+    if (wid >= nrb * W) return;  // uniform per wavefront
+    const int64_t rb = wid / W, w = wid % W;
+    const int64_t row = rb * 64 + lane;
+    const uint32_t word = row < rows ? bits[row * W + w] : 0u;
+    uint64_t mine = 0;
+#pragma unroll
+    for (int b = 0; b < 32; ++b) {
+        const uint64_t m = __ballot((word >> b) & 1u);
+        if (lane == b) mine = m;
+    }
+    if (lane < 32) {
+        uint32_t *dst = out + (w * 32 + lane) * rw + rb * 2;
+        dst[0] = (uint32_t)mine;
+        if (rb * 2 + 1 < rw) dst[1] = (uint32_t)(mine >> 32);
+    }
 }
 
 hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, uint32_t *out, hipStream_t s) {
-    const int64_t n = r * (rows / 32);
+    const int64_t waves = ((rows + 63) / 64) * (r / 32);
     prof_begin(K_TRANSPOSE, s);
-    hipLaunchKernelGGL(transpose_bits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, bits, rows, r, out);
+    hipLaunchKernelGGL(transpose_bits_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, bits, rows, r, out);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
@@ -520,30 +532,32 @@ static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
     return e;
 }
 
-// Tile shapes per kind (measured at M=8192, d=4096, r=512): F1 with 64x128
-// tiles of 1x4 waves (64x32 each, twice as many workgroups as CUs); F2 and
-// B2 (N = d_out or d_in, K = r, an f32 [M][N] output) with 128x256 tiles of
-// 2x4 waves when N is a multiple of 256, else 128x128 tiles of 2x2 waves; DH
-// with 128x128 tiles of 2x2 waves; B1 with 128x128 tiles of 2x4 waves. The
-// kinds with N = d_out or d_in walk groups of 8 M tiles per N tile. Every
-// kind with column partials uses 128-row tiles.
-int gemm_tile_rows(GemmKind kind) { return kind == GEMM_F1 ? 64 : 128; }
+// Tile shapes per kind (measured at M=8192, d=4096, r=512): 64-row tiles of
+// 1x4 waves, two workgroups per CU so that one's prologue and epilogue
+// overlap the other's main loop. F1 and B1 (N = r, K = d) use 64x128 tiles
+// (64x32 per wave). F2, DH and B2 (N = d_out or d_in, K = r) use 64x256
+// tiles (64x64 per wave) when N is a multiple of 256, else 64x128, and walk
+// groups of 8 M tiles per N tile. Every kind uses 64-row tiles, so the
+// column partials have ceil(M/64) rows.
+int gemm_tile_rows(GemmKind) { return 64; }
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     const bool wide = a.N % 256 == 0;
     switch (kind) {
         case GEMM_F1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1>(K_GEMM_F1, a, s);
         case GEMM_F2:
-            return wide ? launch_gemm_t<128, 256, 2, 4, 2, 2, true, true, false, 8>(K_GEMM_F2, a, s)
-                        : launch_gemm_t<128, 128, 2, 2, 2, 2, true, true, false, 8>(K_GEMM_F2, a, s);
+            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, true, true, false, 8>(K_GEMM_F2, a, s)
+                        : launch_gemm_t<64, 128, 1, 4, 2, 2, true, true, false, 8>(K_GEMM_F2, a, s);
         case GEMM_F2_NOTAPE:
-            return wide ? launch_gemm_t<128, 256, 2, 4, 2, 2, false, true, false, 8>(K_GEMM_F2, a, s)
-                        : launch_gemm_t<128, 128, 2, 2, 2, 2, false, true, false, 8>(K_GEMM_F2, a, s);
-        case GEMM_DH: return launch_gemm_t<128, 128, 2, 2, 2, 2, false, false, true, 8>(K_GEMM_DH, a, s);
-        case GEMM_B1: return launch_gemm_t<128, 128, 2, 4, 2, 2, true, false, true, 1>(K_GEMM_B1, a, s);
+            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, false, 8>(K_GEMM_F2, a, s)
+                        : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, false, 8>(K_GEMM_F2, a, s);
+        case GEMM_DH:
+            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, false, true, 8>(K_GEMM_DH, a, s)
+                        : launch_gemm_t<64, 128, 1, 4, 2, 2, false, false, true, 8>(K_GEMM_DH, a, s);
+        case GEMM_B1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, true, 1>(K_GEMM_B1, a, s);
         case GEMM_B2:
-            return wide ? launch_gemm_t<128, 256, 2, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s)
-                        : launch_gemm_t<128, 128, 2, 2, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s);
+            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s)
+                        : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s);
     }
     return hipErrorInvalidValue;
 }
