@@ -74,10 +74,12 @@ Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     off += up((size_t)(r * ((d_in > d_out ? d_in : d_out) / 32)) * 4);
     L.db = off;
     off += up((size_t)(M * r) * 4);
+    // dh and dl partials: one row per 32 tokens covers every producer (the
+    // c-tape column sum, the recomputed-c contraction, B1 with dh fused)
     L.part_h = off;
-    off += up((size_t)(ceil_div(M, COLSUM_ROWS) * d_out) * 4);
+    off += up((size_t)(ceil_div(M, PART_ROWS_MIN) * d_out) * 4);
     L.part_l = off;
-    off += up((size_t)(ceil_div(M, GEMM_BM_MIN) * r) * 4);
+    off += up((size_t)(ceil_div(M, PART_ROWS_MIN) * r) * 4);
     L.part_g = off;
     off += up((size_t)(ceil_div(M, GEMM_BM_MIN) * d_in) * 4);
     L.total = off;
@@ -249,15 +251,18 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     float *part_l = (float *)(ws + L.part_l);
     float *part_g = (float *)(ws + L.part_g);
     const float inv = 1.0f / gscale;  // exact: gscale is a power of two
-    const int64_t mt_b1 = ceil_div(M, gemm_tile_rows(GEMM_B1));
+    const bool fused = tape_c == nullptr && b1dh_cols(r) == r;  // B1 with dh fused
+    const int64_t mt_b1 = ceil_div(M, gemm_tile_rows(fused ? GEMM_B1_DH : GEMM_B1));
     const int64_t mt_b2 = ceil_div(M, gemm_tile_rows(GEMM_B2));
 
     BLR_TRY(launch_transpose_bits(bits_u, d_out, r, bits_ut, s));
 
     // partials of dh = sum_t dy.c: from the stored tape, or with c
     // recomputed by F2's contraction (same tiles, so the same c)
-    int64_t nparts_h;
-    if (tape_c) {
+    int64_t nparts_h = mt_b1;
+    if (fused) {
+        // computed inside B1 below
+    } else if (tape_c) {
         BLR_TRY(launch_colsum(dy, tape_c, M, (int)d_out, part_h, s));
         nparts_h = ceil_div(M, COLSUM_ROWS);
     } else {
@@ -291,7 +296,17 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     b1.out = db;
     b1.dot_other = tape_a;
     b1.dot_partial = part_l;
-    BLR_TRY(launch_gemm(GEMM_B1, b1, s));
+    if (fused) {
+        // and, per 32-column block of dy, c = f16(a.l) S_U^T recomputed and
+        // dh partials sum_t dy.c (c is not stored)
+        b1.dh_bits = bits_u;
+        b1.dh_a = tape_a;
+        b1.dh_l = l;
+        b1.dh_partial = part_h;
+        BLR_TRY(launch_gemm(GEMM_B1_DH, b1, s));
+    } else {
+        BLR_TRY(launch_gemm(GEMM_B1, b1, s));
+    }
 
     // dx' = f16(db.l.gs) S_V^T / gs; dx (+)= g.dx'; dg += sum_t x.dx'
     GemmArgs b2 = {};

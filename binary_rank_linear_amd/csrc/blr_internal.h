@@ -14,6 +14,9 @@ namespace blr {
 constexpr int GEMM_BM_MIN = 64;
 // Tokens per partial of the standalone column reduction.
 constexpr int COLSUM_ROWS = 64;
+// Fewest tokens per row of the dh / dl partial buffers (B1 with dh fused
+// uses 32-row tiles).
+constexpr int PART_ROWS_MIN = 32;
 
 // Kernel kinds, for per-kernel timing.
 enum KernelId {
@@ -26,6 +29,7 @@ enum KernelId {
     K_COLSUM,    // partials of dh = sum_t dy.c from the stored c tape
     K_GEMM_DH,   // c recomputed as in F2, partials of dh = sum_t dy.c
     K_FINISH,    // sum of partials into dh / dl / dg
+    K_GEMM_B1_DH, // B1 with dh fused (c recomputed per column block)
     K_COUNT
 };
 const char *kernel_name(int id);
@@ -48,11 +52,20 @@ struct GemmArgs {
     int out2acc;
     const float *dot_other; // [M][N]: partial[mt][n] = sum_{m in tile} product * other
     float *dot_partial;     // [ceil(M/gemm_tile_rows(kind))][N]
+    // B1 with the dh reduction fused (GEMM_B1_DH): c = (a.l) S_U^T is
+    // recomputed per column block of dy and dh partials sum dy.c over the tile
+    const uint32_t *dh_bits; // bitmap of S_U [K][N/32] (K = d_out, N = r)
+    const float *dh_a;       // the a tape [M][N]
+    const float *dh_l;       // l [N]
+    float *dh_partial;       // [ceil(M/32) * (N/BN)][K]
 };
 
 // F2 writes the c tape and y (F2) or y only (F2_NOTAPE); DH repeats F2's
 // contraction with the same tiles (so c is bit-identical) and sums dy.c.
-enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_F2_NOTAPE, GEMM_B1, GEMM_B2, GEMM_DH };
+enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_F2_NOTAPE, GEMM_B1, GEMM_B2, GEMM_DH, GEMM_B1_DH };
+// Rank columns per workgroup of GEMM_B1_DH (512, 256 or 128; the dh
+// partials have ceil(M/32) * (r / b1dh_cols(r)) rows).
+int b1dh_cols(int64_t r);
 
 // Sign-plane expansion jobs (one bitmap each; pl and/or plt may be null).
 struct ExpandJob {

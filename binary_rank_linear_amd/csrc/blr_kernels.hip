@@ -246,7 +246,7 @@ hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, 
     return e;
 }
 
-template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM>
+template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false>
 __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     constexpr int NT = WM * WN * 64;
     constexpr int BK = 32;          // one bitmap word per plane row per step
@@ -259,10 +259,14 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     constexpr int PER = BM / RPP;   // float4 per thread per stage
     static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % RPP == 0 && PER >= 1, "tile shape");
     static_assert(4 % P == 0, "the register ring must divide the 4-step unroll");
-    static_assert(NT >= BN, "one thread per column for the column partials");
+    // Fused dh (B1 only): 32-row tiles, one row of waves, 128 ranks per wave.
+    static_assert(!FDH || (BM == 32 && WM == 1 && TN == 128 && DOT && OUT), "fused dh shape");
+    constexpr int LDR = 36;         // floats per row of the transposed f32 dy tile (pad: conflict-free)
 
     __shared__ __attribute__((aligned(16))) _Float16 As[NS * BM * LDK];
     __shared__ float red[DOT ? WM * BN : 1];
+    __shared__ __attribute__((aligned(16))) float dyT[FDH ? NS * 32 * LDR : 1];  // [buf][column][row]
+    __shared__ float redh[FDH ? 2 * WN * 32 : 1];                                // [step & 1][wave][column]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -326,6 +330,35 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     asm volatile("v_mov_b32 %0, 0x80008000" : "=v"(sgnmask));
     asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one16));
 
+    // Fused dh: the wave's A fragments f16(a * l) for its 128 ranks stay in
+    // registers (rows past M are zero, so they add nothing to dh), and each
+    // step reads the bitmap words of S_U rows i0 + (lane % 32), ranks of the
+    // wave: 4 words, one 16-byte load.
+    half8_t al[FDH ? 8 : 1];
+    uint32_t hoff = 0;
+    const __amdgpu_buffer_rsrc_t rH = make_rsrc(p.dh_bits, FDH ? (uint64_t)K * N / 8 : 0);
+    if (FDH) {
+        const int64_t gm = m0 + (lane & 31);
+        const bool inr = gm < M;
+        const float *ar_ = p.dh_a + (inr ? gm : 0) * N;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int k = n0 + wn * TN + 16 * t + 8 * (lane >> 5);
+            const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(ar_ + k);
+            const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(ar_ + k + 4);
+            const f32x4_t l0 = *reinterpret_cast<const f32x4_t *>(p.dh_l + k);
+            const f32x4_t l1 = *reinterpret_cast<const f32x4_t *>(p.dh_l + k + 4);
+            half8_t h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h[e] = inr ? (_Float16)(x0[e] * l0[e]) : (_Float16)0.0f;
+                h[4 + e] = inr ? (_Float16)(x1[e] * l1[e]) : (_Float16)0.0f;
+            }
+            al[t] = h;
+        }
+        hoff = (uint32_t)(((lane & 31) * (N / 32) + (n0 + wn * TN) / 32) * 4);
+    }
+
     f32x16_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -364,6 +397,13 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
             h_.x = f16x2_scaled(ar[q][v].x, cs_.x, ar[q][v].y, cs_.y);                     \
             h_.y = f16x2_scaled(ar[q][v].z, cs_.z, ar[q][v].w, cs_.w);                     \
             *reinterpret_cast<uint2 *>(dst_ + v * RPP * LDK) = h_;                          \
+            if (FDH) {                                                                     \
+                const int r_ = arow + v * RPP;                                             \
+                const bool in_ = m0 + r_ < M;                                              \
+                float *dt_ = dyT + (buf) * (32 * LDR) + r_;                                \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e)                              \
+                    dt_[(4 * c4 + e) * LDR] = in_ ? ar[q][v][e] : 0.0f;                    \
+            }                                                                              \
         }                                                                                  \
     } while (0)
 
@@ -390,6 +430,40 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
                     __builtin_amdgcn_mfma_f32_32x32x16_f16(a_[i][s], b_[j][s], acc[i][j], 0, 0, 0); \
     } while (0)
 
+    // Fused dh, step kt (columns i0 = 32 kt of d_out): the wave's partial
+    // c over its ranks (8 MFMAs into two accumulators), times the f32 dy of
+    // the step, summed over the tile's rows; the two lane groups add, and
+    // the waves' sums go to redh for wave 0 to add in wave order after the
+    // step's barrier (dh is linear in c, so per-wave partial c suffice).
+#define BLR_DH(HB, BUF, KT)                                                                \
+    do {                                                                                   \
+        f32x16_t c0_, c1_;                                                                 \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) c0_[v] = c1_[v] = 0.0f;             \
+        _Pragma("unroll") for (int t = 0; t < 8; t += 2) {                                 \
+            c0_ = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[t], sign_frag(HB[t / 2], sel[0], sgnmask, one16), c0_, 0, 0, 0); \
+            c1_ = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[t + 1], sign_frag(HB[t / 2], sel[1], sgnmask, one16), c1_, 0, 0, 0); \
+        }                                                                                  \
+        const float *dt_ = dyT + (BUF) * (32 * LDR) + (lane & 31) * LDR + 4 * (lane >> 5); \
+        float ds_ = 0.0f;                                                                  \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                    \
+            const f32x4_t d4_ = *reinterpret_cast<const f32x4_t *>(dt_ + 8 * q);           \
+            _Pragma("unroll") for (int e = 0; e < 4; ++e) ds_ += (c0_[4 * q + e] + c1_[4 * q + e]) * d4_[e]; \
+        }                                                                                  \
+        ds_ += __shfl_xor(ds_, 32);                                                        \
+        if (lane < 32) redh[((KT) & 1) * (WN * 32) + wn * 32 + lane] = ds_;                \
+    } while (0)
+    // wave 0 adds the waves' dh sums of step KT (after that step's barrier);
+    // the fragments hold -S, hence the sign
+#define BLR_DH_STORE(KT)                                                                   \
+    do {                                                                                   \
+        if (wave == 0 && lane < 32) {                                                      \
+            const float *rr_ = redh + ((KT) & 1) * (WN * 32);                              \
+            float s_ = 0.0f;                                                               \
+            _Pragma("unroll") for (int w = 0; w < WN; ++w) s_ += rr_[w * 32 + lane];       \
+            p.dh_partial[((int64_t)mt * ntn + nt) * K + (int64_t)(KT) * 32 + lane] = -s_;  \
+        }                                                                                  \
+    } while (0)
+
     // Prologue: stages 0 and 1 into LDS buffers 0 and 1, the register ring
     // refilled behind them, the bitmap words of groups 0 and 1, and the
     // fragments of step 0.
@@ -404,7 +478,9 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     __syncthreads();
     BLR_AFRAG(fa, 0);
     BLR_BFRAG(fb, bq, 0);
-    int b1 = 1, b2 = 2;  // LDS buffers of steps kt+1 and kt+2
+    int b0 = 0, b1 = 1, b2 = 2;  // LDS buffers of steps kt, kt+1 and kt+2
+    u32x4_t hb[2];               // dh bitmap words of steps kt and kt+1
+    if (FDH) hb[0] = load_u32x4(rH, hoff, 0);
 
     // Iteration kt: fragments of step kt+1 are read and decoded while the
     // MFMAs of step kt run, stage kt+2 goes to LDS and stage kt+2+P is
@@ -416,6 +492,11 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int kt = kt0 + u;
+            if (FDH) {
+                const int kn_ = kt + 1 < nk ? kt + 1 : nk - 1;
+                hb[(u + 1) & 1] = load_u32x4(rH, hoff, (uint32_t)kn_ * N * 4);
+                if (kt > 0) BLR_DH_STORE(kt - 1);
+            }
             if (u % 2 == 0) {
                 BLR_AFRAG(fa2, b1);
                 BLR_BFRAG(fb2, bq, u + 1);
@@ -429,6 +510,7 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
                 }
                 BLR_MMA(fa2, fb2);
             }
+            if (FDH) BLR_DH(hb[u & 1], b0, kt);
             if (u == 3) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) bq[j] = bn[j];
@@ -440,10 +522,17 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
             // keep later steps' work out of this one: hoisted above the
             // barrier it would wait for loads issued just before
             __builtin_amdgcn_sched_barrier(0);
+            b0 = b1;
             b1 = b2;
             b2 = b2 == NS - 1 ? 0 : b2 + 1;
         }
     }
+    if (FDH) {
+        __syncthreads();
+        BLR_DH_STORE(nk - 1);
+    }
+#undef BLR_DH
+#undef BLR_DH_STORE
 #undef BLR_GLOAD
 #undef BLR_BLOAD
 #undef BLR_SSTORE
@@ -511,21 +600,21 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
             if (lane < 32) red[wm * BN + wn * TN + j * 32 + lane] = dsum[j];
         }
         __syncthreads();
-        if (tid < BN) {
+        for (int c = tid; c < BN; c += NT) {
             float sum = 0.0f;
 #pragma unroll
-            for (int w = 0; w < WM; ++w) sum += red[w * BN + tid];
-            p.dot_partial[(int64_t)mt * N + n0 + tid] = sum;
+            for (int w = 0; w < WM; ++w) sum += red[w * BN + c];
+            p.dot_partial[(int64_t)mt * N + n0 + c] = sum;
         }
     }
 }
 
-template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM>
+template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false>
 static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
     if (a.N % BN != 0 || a.K % 128 != 0 || a.K < 128) return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)(a.N / BN) * ((a.M + BM - 1) / BM);
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM, FDH>), dim3((unsigned)tiles),
                        dim3(WM * WN * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     prof_end(s);
@@ -539,7 +628,8 @@ static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
 // tiles (64x64 per wave) when N is a multiple of 256, else 64x128, and walk
 // groups of 8 M tiles per N tile. Every kind uses 64-row tiles, so the
 // column partials have ceil(M/64) rows.
-int gemm_tile_rows(GemmKind) { return 64; }
+int gemm_tile_rows(GemmKind kind) { return kind == GEMM_B1_DH ? 32 : 64; }
+int b1dh_cols(int64_t r) { return (r == 128 || r == 256 || r == 512) ? (int)r : 0; }
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     const bool wide = a.N % 256 == 0;
@@ -558,6 +648,13 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
         case GEMM_B2:
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s);
+        case GEMM_B1_DH:
+            switch (a.N) {  // one workgroup covers every rank: r / 128 waves (1, 2 or 4)
+                case 128: return launch_gemm_t<32, 128, 1, 1, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
+                case 256: return launch_gemm_t<32, 256, 1, 2, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
+                case 512: return launch_gemm_t<32, 512, 1, 4, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
+            }
+            return hipErrorInvalidValue;
     }
     return hipErrorInvalidValue;
 }
@@ -656,6 +753,7 @@ const char *kernel_name(int id) {
         case K_COLSUM: return "colsum_dy_c";
         case K_GEMM_DH: return "gemm_dh_recompute_c";
         case K_FINISH: return "colsum_finish";
+        case K_GEMM_B1_DH: return "gemm_b1_dh_fused";
     }
     return "?";
 }
