@@ -47,6 +47,8 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
         return M * (r + do) * f32 + do * r / 8 + r * f32, 2.0 * M * do * r
     if name == "gemm_b1_dyh_su":     # read dy and a, write db
         return M * (do + 2 * r) * f32 + r * do / 8 + do * f32, 2.0 * M * r * do
+    if name == "gemm_b1_dh_fused":   # read dy and a, write db; B1 plus c recomputed for dh (two contractions)
+        return M * (do + 2 * r) * f32 + 2 * r * do / 8 + do * f32 + r * f32, 4.0 * M * r * do
     if name == "gemm_b2_dbl_svt":    # read db and x, write dx
         return M * (r + 2 * di) * f32 + di * r / 8 + (r + di) * f32, 2.0 * M * di * r
     if name == "colsum_dy_c":        # read dy and c

@@ -247,8 +247,8 @@ hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, 
 }
 
 template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false>
-__global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
-    constexpr int NT = WM * WN * 64;
+__global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kernel(GemmArgs p) {
+    constexpr int NT = WM * WN * 64;  // threads of the contraction role
     constexpr int BK = 32;          // one bitmap word per plane row per step
     constexpr int LDK = BK + 8;     // halves per LDS row (pad: conflict-free 16-byte reads)
     constexpr int NS = 3;           // LDS ring depth
@@ -259,7 +259,10 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     constexpr int PER = BM / RPP;   // float4 per thread per stage
     static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % RPP == 0 && PER >= 1, "tile shape");
     static_assert(4 % P == 0, "the register ring must divide the 4-step unroll");
-    // Fused dh (B1 only): 32-row tiles, one row of waves, 128 ranks per wave.
+    // Fused dh (B1 only): 32-row tiles, one row of waves, 128 ranks per wave,
+    // and as many more waves in a second role (DH waves): they stage the f32
+    // dy tile and compute the dh partials, so each SIMD holds one wave of
+    // each role and one's VALU work overlaps the other's MFMAs.
     static_assert(!FDH || (BM == 32 && WM == 1 && TN == 128 && DOT && OUT), "fused dh shape");
     constexpr int LDR = 36;         // floats per row of the transposed f32 dy tile (pad: conflict-free)
 
@@ -271,7 +274,9 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
+    const bool dhw = FDH && wave >= WM * WN;         // DH-role wave (uniform)
+    const int rwave = dhw ? wave - WM * WN : wave;   // index within the role
+    const int wm = rwave / WN, wn = rwave % WN;
     const int N = p.N, K = p.K;
     const int ntn = N / BN;
     const int L = blockIdx.x, G = gridDim.x;
@@ -301,7 +306,8 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     // checked by the caller). Rows past M read row M-1 instead: a row of the
     // product depends on its own A row only, and those rows are never stored
     // or summed.
-    const int c4 = tid % TPR, arow = tid / TPR;
+    const int st = dhw ? tid - NT : tid;  // staging thread index within the role
+    const int c4 = st % TPR, arow = st / TPR;
     uint32_t aoff[PER];
 #pragma unroll
     for (int v = 0; v < PER; ++v) {
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     half8_t al[FDH ? 8 : 1];
     uint32_t hoff = 0;
     const __amdgpu_buffer_rsrc_t rH = make_rsrc(p.dh_bits, FDH ? (uint64_t)K * N / 8 : 0);
-    if (FDH) {
+    if (dhw) {
         const int64_t gm = m0 + (lane & 31);
         const bool inr = gm < M;
         const float *ar_ = p.dh_a + (inr ? gm : 0) * N;
@@ -390,19 +396,23 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
 
 #define BLR_SSTORE(q, buf)                                                                 \
     do {                                                                                   \
-        const f32x4_t cs_ = cr[q] * p.ascale;                                              \
-        _Float16 *dst_ = As + (buf) * (BM * LDK) + wofs;                                   \
-        _Pragma("unroll") for (int v = 0; v < PER; ++v) {                                  \
-            uint2 h_;                                                                      \
-            h_.x = f16x2_scaled(ar[q][v].x, cs_.x, ar[q][v].y, cs_.y);                     \
-            h_.y = f16x2_scaled(ar[q][v].z, cs_.z, ar[q][v].w, cs_.w);                     \
-            *reinterpret_cast<uint2 *>(dst_ + v * RPP * LDK) = h_;                          \
-            if (FDH) {                                                                     \
+        if (dhw) {                                                                         \
+            /* DH role: the f32 dy tile, transposed, rows past M zero */                   \
+            _Pragma("unroll") for (int v = 0; v < PER; ++v) {                              \
                 const int r_ = arow + v * RPP;                                             \
                 const bool in_ = m0 + r_ < M;                                              \
                 float *dt_ = dyT + (buf) * (32 * LDR) + r_;                                \
                 _Pragma("unroll") for (int e = 0; e < 4; ++e)                              \
                     dt_[(4 * c4 + e) * LDR] = in_ ? ar[q][v][e] : 0.0f;                    \
+            }                                                                              \
+        } else {                                                                           \
+            const f32x4_t cs_ = cr[q] * p.ascale;                                          \
+            _Float16 *dst_ = As + (buf) * (BM * LDK) + wofs;                               \
+            _Pragma("unroll") for (int v = 0; v < PER; ++v) {                              \
+                uint2 h_;                                                                  \
+                h_.x = f16x2_scaled(ar[q][v].x, cs_.x, ar[q][v].y, cs_.y);                 \
+                h_.y = f16x2_scaled(ar[q][v].z, cs_.z, ar[q][v].w, cs_.w);                 \
+                *reinterpret_cast<uint2 *>(dst_ + v * RPP * LDK) = h_;                      \
             }                                                                              \
         }                                                                                  \
     } while (0)
@@ -433,8 +443,9 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     // Fused dh, step kt (columns i0 = 32 kt of d_out): the wave's partial
     // c over its ranks (8 MFMAs into two accumulators), times the f32 dy of
     // the step, summed over the tile's rows; the two lane groups add, and
-    // the waves' sums go to redh for wave 0 to add in wave order after the
-    // step's barrier (dh is linear in c, so per-wave partial c suffice).
+    // the waves' sums go to redh for the first DH wave to add in wave order
+    // after the step's barrier (dh is linear in c, so per-wave partial c
+    // suffice).
 #define BLR_DH(HB, BUF, KT)                                                                \
     do {                                                                                   \
         f32x16_t c0_, c1_;                                                                 \
@@ -452,11 +463,12 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
         ds_ += __shfl_xor(ds_, 32);                                                        \
         if (lane < 32) redh[((KT) & 1) * (WN * 32) + wn * 32 + lane] = ds_;                \
     } while (0)
-    // wave 0 adds the waves' dh sums of step KT (after that step's barrier);
+    // the first DH wave adds the waves' dh sums of step KT (after that
+    // step's barrier);
     // the fragments hold -S, hence the sign
 #define BLR_DH_STORE(KT)                                                                   \
     do {                                                                                   \
-        if (wave == 0 && lane < 32) {                                                      \
+        if (dhw && rwave == 0 && lane < 32) {                                              \
             const float *rr_ = redh + ((KT) & 1) * (WN * 32);                              \
             float s_ = 0.0f;                                                               \
             _Pragma("unroll") for (int w = 0; w < WN; ++w) s_ += rr_[w * 32 + lane];       \
@@ -469,18 +481,23 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     // fragments of step 0.
 #pragma unroll
     for (int q = 0; q < P; ++q) BLR_GLOAD(q, q);
-    BLR_BLOAD(bq, 0);
-    BLR_BLOAD(bn, 1);
+    if (!dhw) {
+        BLR_BLOAD(bq, 0);
+        BLR_BLOAD(bn, 1);
+    }
     BLR_SSTORE(0, 0);
     BLR_GLOAD(0, P);
     BLR_SSTORE(1 % P, 1);
     BLR_GLOAD(1 % P, P + 1);
     __syncthreads();
-    BLR_AFRAG(fa, 0);
-    BLR_BFRAG(fb, bq, 0);
-    int b0 = 0, b1 = 1, b2 = 2;  // LDS buffers of steps kt, kt+1 and kt+2
     u32x4_t hb[2];               // dh bitmap words of steps kt and kt+1
-    if (FDH) hb[0] = load_u32x4(rH, hoff, 0);
+    if (dhw) {
+        hb[0] = load_u32x4(rH, hoff, 0);
+    } else {
+        BLR_AFRAG(fa, 0);
+        BLR_BFRAG(fb, bq, 0);
+    }
+    int b0 = 0, b1 = 1, b2 = 2;  // LDS buffers of steps kt, kt+1 and kt+2
 
     // Iteration kt: fragments of step kt+1 are read and decoded while the
     // MFMAs of step kt run, stage kt+2 goes to LDS and stage kt+2+P is
@@ -488,48 +505,62 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     // loads are unconditional (stages and groups past the end re-read the
     // last one and are never multiplied), so the compiler counts outstanding
     // loads exactly and waits only for the stage it converts.
-    for (int kt0 = 0; kt0 < nk; kt0 += 4) {
+    if (dhw) {
+        // DH role: per step the partial c of the wave's ranks and its dh sums
+        for (int kt0 = 0; kt0 < nk; kt0 += 4) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int kt = kt0 + u;
-            if (FDH) {
+            for (int u = 0; u < 4; ++u) {
+                const int kt = kt0 + u;
                 const int kn_ = kt + 1 < nk ? kt + 1 : nk - 1;
                 hb[(u + 1) & 1] = load_u32x4(rH, hoff, (uint32_t)kn_ * N * 4);
                 if (kt > 0) BLR_DH_STORE(kt - 1);
+                BLR_DH(hb[u & 1], b0, kt);
+                BLR_SSTORE((u + 2) % P, b2);
+                BLR_GLOAD((u + 2) % P, kt + 2 + P);
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+                b0 = b1;
+                b1 = b2;
+                b2 = b2 == NS - 1 ? 0 : b2 + 1;
             }
-            if (u % 2 == 0) {
-                BLR_AFRAG(fa2, b1);
-                BLR_BFRAG(fb2, bq, u + 1);
-                BLR_MMA(fa, fb);
-            } else {
-                BLR_AFRAG(fa, b1);
-                if (u < 3) {
-                    BLR_BFRAG(fb, bq, u + 1);
-                } else {
-                    BLR_BFRAG(fb, bn, 0);
-                }
-                BLR_MMA(fa2, fb2);
-            }
-            if (FDH) BLR_DH(hb[u & 1], b0, kt);
-            if (u == 3) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j) bq[j] = bn[j];
-                BLR_BLOAD(bn, kt0 / 4 + 2);
-            }
-            BLR_SSTORE((u + 2) % P, b2);
-            BLR_GLOAD((u + 2) % P, kt + 2 + P);
-            __syncthreads();
-            // keep later steps' work out of this one: hoisted above the
-            // barrier it would wait for loads issued just before
-            __builtin_amdgcn_sched_barrier(0);
-            b0 = b1;
-            b1 = b2;
-            b2 = b2 == NS - 1 ? 0 : b2 + 1;
         }
-    }
-    if (FDH) {
         __syncthreads();
         BLR_DH_STORE(nk - 1);
+    } else {
+        for (int kt0 = 0; kt0 < nk; kt0 += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int kt = kt0 + u;
+                if (u % 2 == 0) {
+                    BLR_AFRAG(fa2, b1);
+                    BLR_BFRAG(fb2, bq, u + 1);
+                    BLR_MMA(fa, fb);
+                } else {
+                    BLR_AFRAG(fa, b1);
+                    if (u < 3) {
+                        BLR_BFRAG(fb, bq, u + 1);
+                    } else {
+                        BLR_BFRAG(fb, bn, 0);
+                    }
+                    BLR_MMA(fa2, fb2);
+                }
+                if (u == 3) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) bq[j] = bn[j];
+                    BLR_BLOAD(bn, kt0 / 4 + 2);
+                }
+                BLR_SSTORE((u + 2) % P, b2);
+                BLR_GLOAD((u + 2) % P, kt + 2 + P);
+                __syncthreads();
+                // keep later steps' work out of this one: hoisted above the
+                // barrier it would wait for loads issued just before
+                __builtin_amdgcn_sched_barrier(0);
+                b0 = b1;
+                b1 = b2;
+                b2 = b2 == NS - 1 ? 0 : b2 + 1;
+            }
+        }
+        if (FDH) __syncthreads();  // matches the DH role's final barrier
     }
 #undef BLR_DH
 #undef BLR_DH_STORE
@@ -584,23 +615,27 @@ __global__ __launch_bounds__(WM *WN * 64, MINB) void gemm_kernel(GemmArgs p) {
             }                                                                              \
         }                                                                                  \
     } while (0)
-    if (full) {
-        BLR_EPI_BLOCK(false);
-    } else {
-        BLR_EPI_BLOCK(true);
+    if (!dhw) {
+        if (full) {
+            BLR_EPI_BLOCK(false);
+        } else {
+            BLR_EPI_BLOCK(true);
+        }
     }
 #undef BLR_EPI_BLOCK
 #undef BLR_UOFF
     if (DOT) {
         // lanes l and l+32 hold the same columns; then the WM waves of a
         // column strip add in row order
+        if (!dhw) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            dsum[j] += __shfl_xor(dsum[j], 32);
-            if (lane < 32) red[wm * BN + wn * TN + j * 32 + lane] = dsum[j];
+            for (int j = 0; j < FN; ++j) {
+                dsum[j] += __shfl_xor(dsum[j], 32);
+                if (lane < 32) red[wm * BN + wn * TN + j * 32 + lane] = dsum[j];
+            }
         }
         __syncthreads();
-        for (int c = tid; c < BN; c += NT) {
+        for (int c = tid; c < BN && tid < NT; c += NT) {
             float sum = 0.0f;
 #pragma unroll
             for (int w = 0; w < WM; ++w) sum += red[w * BN + c];
@@ -615,7 +650,7 @@ static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
     const int64_t tiles = (int64_t)(a.N / BN) * ((a.M + BM - 1) / BM);
     prof_begin(id, s);
     hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM, FDH>), dim3((unsigned)tiles),
-                       dim3(WM * WN * 64), 0, s, a);
+                       dim3((FDH ? 2 : 1) * WM * WN * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
@@ -649,10 +684,10 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s);
         case GEMM_B1_DH:
-            switch (a.N) {  // one workgroup covers every rank: r / 128 waves (1, 2 or 4)
-                case 128: return launch_gemm_t<32, 128, 1, 1, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
-                case 256: return launch_gemm_t<32, 256, 1, 2, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
-                case 512: return launch_gemm_t<32, 512, 1, 4, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
+            switch (a.N) {  // one workgroup covers every rank: r / 128 waves of each role (1, 2 or 4)
+                case 128: return launch_gemm_t<32, 128, 1, 1, 1, 2, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
+                case 256: return launch_gemm_t<32, 256, 1, 2, 1, 2, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
+                case 512: return launch_gemm_t<32, 512, 1, 4, 1, 2, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
             }
             return hipErrorInvalidValue;
     }
