@@ -246,10 +246,12 @@ hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, 
     return e;
 }
 
-template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false>
+template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false,
+          int KB = 2>
 __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     constexpr int NT = WM * WN * 64;  // threads of the contraction role
-    constexpr int BK = 32;          // one bitmap word per plane row per step
+    constexpr int BK = 16 * KB;     // k per step: KB MFMA k-blocks, KB/2 bitmap words per plane row
+    constexpr int U = 8 / KB;       // steps per group of 4 bitmap words (the loop unroll)
     constexpr int LDK = BK + 8;     // halves per LDS row (pad: conflict-free 16-byte reads)
     constexpr int NS = 3;           // LDS ring depth
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -258,7 +260,8 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     constexpr int RPP = NT / TPR;   // activation rows per pass
     constexpr int PER = BM / RPP;   // float4 per thread per stage
     static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % RPP == 0 && PER >= 1, "tile shape");
-    static_assert(4 % P == 0, "the register ring must divide the 4-step unroll");
+    static_assert((KB == 2 || KB == 4) && U % P == 0, "the register ring must divide the unroll");
+    static_assert(!FDH || KB == 2, "fused dh walks 32-column steps");
     // Fused dh (B1 only): 32-row tiles, one row of waves, 128 ranks per wave,
     // and as many more waves in a second role (DH waves): they stage the f32
     // dy tile and compute the dh partials, so each SIMD holds one wave of
@@ -298,7 +301,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     }
     const int n0 = nt * BN;
     const int64_t m0 = (int64_t)mt * BM;
-    const int nk = K / BK;  // a multiple of 4 (the launcher checks)
+    const int nk = K / BK;  // a multiple of U (K is a multiple of 128)
     const int64_t M = p.M;
 
     // Activation addressing: a uniform base advanced by the stage, plus a
@@ -376,8 +379,8 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     f32x4_t ar[P][PER];
     f32x4_t cr[P];
     u32x4_t bq[FN], bn[FN];  // bitmap words: this 4-step group, the next
-    half8_t fa[FM][2], fb[FN][2];
-    half8_t fa2[FM][2], fb2[FN][2];
+    half8_t fa[FM][KB], fb[FN][KB];
+    half8_t fa2[FM][KB], fb2[FN][KB];
 
 #define BLR_GLOAD(q, kt)                                                                   \
     do {                                                                                   \
@@ -389,7 +392,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 
 #define BLR_BLOAD(dst, grp4)                                                               \
     do {                                                                                   \
-        const int g_ = (grp4) < nk / 4 ? (grp4) : nk / 4 - 1;                              \
+        const int g_ = (grp4) < nk / U ? (grp4) : nk / U - 1;                              \
         _Pragma("unroll") for (int j = 0; j < FN; ++j) dst[j] =                            \
             load_u32x4(rB, boff[j], (uint32_t)g_ * 16);                                    \
     } while (0)
@@ -421,20 +424,20 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     do {                                                                                   \
         const _Float16 *src_ = As + (buf) * (BM * LDK) + rofs;                             \
         _Pragma("unroll") for (int i = 0; i < FM; ++i)                                     \
-            _Pragma("unroll") for (int s = 0; s < 2; ++s) dst[i][s] =                      \
+            _Pragma("unroll") for (int s = 0; s < KB; ++s) dst[i][s] =                     \
                 *reinterpret_cast<const half8_t *>(src_ + i * 32 * LDK + s * 16);          \
     } while (0)
 
 #define BLR_BFRAG(dst, words, u)                                                           \
     do {                                                                                   \
         _Pragma("unroll") for (int j = 0; j < FN; ++j)                                     \
-            _Pragma("unroll") for (int s = 0; s < 2; ++s) dst[j][s] =                      \
-                sign_frag(words[j][u], sel[s], sgnmask, one16);                            \
+            _Pragma("unroll") for (int s = 0; s < KB; ++s) dst[j][s] =                     \
+                sign_frag(words[j][(u) * (KB / 2) + s / 2], sel[s % 2], sgnmask, one16);   \
     } while (0)
 
 #define BLR_MMA(a_, b_)                                                                    \
     do {                                                                                   \
-        _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
+        _Pragma("unroll") for (int s = 0; s < KB; ++s)                                     \
             _Pragma("unroll") for (int i = 0; i < FM; ++i)                                 \
                 _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] =                 \
                     __builtin_amdgcn_mfma_f32_32x32x16_f16(a_[i][s], b_[j][s], acc[i][j], 0, 0, 0); \
@@ -527,9 +530,9 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         __syncthreads();
         BLR_DH_STORE(nk - 1);
     } else {
-        for (int kt0 = 0; kt0 < nk; kt0 += 4) {
+        for (int kt0 = 0; kt0 < nk; kt0 += U) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int kt = kt0 + u;
                 if (u % 2 == 0) {
                     BLR_AFRAG(fa2, b1);
@@ -537,17 +540,17 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                     BLR_MMA(fa, fb);
                 } else {
                     BLR_AFRAG(fa, b1);
-                    if (u < 3) {
+                    if (u < U - 1) {
                         BLR_BFRAG(fb, bq, u + 1);
                     } else {
                         BLR_BFRAG(fb, bn, 0);
                     }
                     BLR_MMA(fa2, fb2);
                 }
-                if (u == 3) {
+                if (u == U - 1) {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) bq[j] = bn[j];
-                    BLR_BLOAD(bn, kt0 / 4 + 2);
+                    BLR_BLOAD(bn, kt0 / U + 2);
                 }
                 BLR_SSTORE((u + 2) % P, b2);
                 BLR_GLOAD((u + 2) % P, kt + 2 + P);
@@ -644,12 +647,13 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     }
 }
 
-template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false>
+template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false,
+          int KB = 2>
 static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
     if (a.N % BN != 0 || a.K % 128 != 0 || a.K < 128) return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)(a.N / BN) * ((a.M + BM - 1) / BM);
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM, FDH>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM, FDH, KB>), dim3((unsigned)tiles),
                        dim3((FDH ? 2 : 1) * WM * WN * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     prof_end(s);
@@ -658,7 +662,8 @@ static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
 
 // Tile shapes per kind (measured at M=8192, d=4096, r=512): 64-row tiles of
 // 1x4 waves, two workgroups per CU so that one's prologue and epilogue
-// overlap the other's main loop. F1 and B1 (N = r, K = d) use 64x128 tiles
+// overlap the other's main loop, and K steps of 64 (one barrier per 4 MFMA
+// k-blocks). F1 and B1 (N = r, K = d) use 64x128 tiles
 // (64x32 per wave). F2, DH and B2 (N = d_out or d_in, K = r) use 64x256
 // tiles (64x64 per wave) when N is a multiple of 256, else 64x128, and walk
 // groups of 8 M tiles per N tile. Every kind uses 64-row tiles, so the
@@ -669,20 +674,20 @@ int b1dh_cols(int64_t r) { return (r == 128 || r == 256 || r == 512) ? (int)r : 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     const bool wide = a.N % 256 == 0;
     switch (kind) {
-        case GEMM_F1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1>(K_GEMM_F1, a, s);
+        case GEMM_F1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
         case GEMM_F2:
-            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, true, true, false, 8>(K_GEMM_F2, a, s)
-                        : launch_gemm_t<64, 128, 1, 4, 2, 2, true, true, false, 8>(K_GEMM_F2, a, s);
+            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, true, true, false, 8, false, 4>(K_GEMM_F2, a, s)
+                        : launch_gemm_t<64, 128, 1, 4, 2, 2, true, true, false, 8, false, 4>(K_GEMM_F2, a, s);
         case GEMM_F2_NOTAPE:
-            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, false, 8>(K_GEMM_F2, a, s)
-                        : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, false, 8>(K_GEMM_F2, a, s);
+            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, false, 8, false, 4>(K_GEMM_F2, a, s)
+                        : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, false, 8, false, 4>(K_GEMM_F2, a, s);
         case GEMM_DH:
-            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, false, true, 8>(K_GEMM_DH, a, s)
-                        : launch_gemm_t<64, 128, 1, 4, 2, 2, false, false, true, 8>(K_GEMM_DH, a, s);
-        case GEMM_B1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, true, 1>(K_GEMM_B1, a, s);
+            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s)
+                        : launch_gemm_t<64, 128, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s);
+        case GEMM_B1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
         case GEMM_B2:
-            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s)
-                        : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8>(K_GEMM_B2, a, s);
+            return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s)
+                        : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s);
         case GEMM_B1_DH:
             switch (a.N) {  // one workgroup covers every rank: r / 128 waves of each role (1, 2 or 4)
                 case 128: return launch_gemm_t<32, 128, 1, 1, 1, 2, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
@@ -733,42 +738,48 @@ hipError_t launch_colsum(const float *A, const float *B, int64_t M, int N, float
 }
 
 // out[n] += sum over parts of partial[part][n], for up to three vectors in
-// one launch (each workgroup owns 64 columns of one job; its 4 waves take
-// every 4th part in order, then the 4 wave sums are added in wave order: a
-// fixed order, so results are deterministic).
+// one launch. Each workgroup owns 32 columns of one job; its 8 groups of 32
+// lanes take every 8th part, 16 loads in flight at a time, each adding its
+// parts in order; then the 8 group sums are added in group order. The order
+// is fixed, so results are deterministic.
+constexpr int FIN_COLS = 32;
 __global__ __launch_bounds__(256) void finish_kernel(FinishJobs jobs) {
-    __shared__ float red[4][64];
+    __shared__ float red[8][FIN_COLS];
     int b = blockIdx.x, j = 0;
     while (j + 1 < jobs.count && b >= jobs.blocks_before[j + 1]) ++j;
     const FinishJob &jb = jobs.job[j];
     const float *__restrict__ partial = jb.partial;
     const int64_t nparts = jb.nparts;
     const int N = jb.N;
-    const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
-    const int col = (b - jobs.blocks_before[j]) * 64 + c;
+    const int c = threadIdx.x & (FIN_COLS - 1), q = threadIdx.x / FIN_COLS;
+    const int col = (b - jobs.blocks_before[j]) * FIN_COLS + c;
     float s = 0.0f;
     if (col < N) {
         int64_t pi = q;
-        for (; pi + 12 < nparts; pi += 16) {
-            const float v0 = partial[pi * N + col], v1 = partial[(pi + 4) * N + col];
-            const float v2 = partial[(pi + 8) * N + col], v3 = partial[(pi + 12) * N + col];
-            s += v0;
-            s += v1;
-            s += v2;
-            s += v3;
+        for (; pi + 15 * 8 < nparts; pi += 16 * 8) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = partial[(pi + 8 * u) * N + col];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) s += v[u];
         }
-        for (; pi < nparts; pi += 4) s += partial[pi * N + col];
+        for (; pi < nparts; pi += 8) s += partial[pi * N + col];
     }
     red[q][c] = s;
     __syncthreads();
-    if (q == 0 && col < N) jb.out[col] = jb.out[col] + (((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
+    if (q == 0 && col < N) {
+        float t = red[0][c];
+#pragma unroll
+        for (int g = 1; g < 8; ++g) t += red[g][c];
+        jb.out[col] = jb.out[col] + t;
+    }
 }
 
 hipError_t launch_finish(FinishJobs jobs, hipStream_t s) {
     int total = 0;
     for (int j = 0; j < jobs.count; ++j) {
         jobs.blocks_before[j] = total;
-        total += (jobs.job[j].N + 63) / 64;
+        total += (jobs.job[j].N + FIN_COLS - 1) / FIN_COLS;
     }
     prof_begin(K_FINISH, s);
     hipLaunchKernelGGL(finish_kernel, dim3((unsigned)total), dim3(256), 0, s, jobs);
