@@ -53,6 +53,8 @@ def _load():
         lib.oracle_blr_forward.restype = i32
         lib.oracle_blr_backward.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, i32]
         lib.oracle_blr_backward.restype = i32
+        lib.oracle_blr_sign_grads.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, i32]
+        lib.oracle_blr_sign_grads.restype = i32
         _lib = lib
     return _lib
 
@@ -137,6 +139,27 @@ def backward(x, dy, bits_u, bits_v, h, l, g, dh0=None, dl0=None, dg0=None, dx0=N
     if rc != 0:
         raise MemoryError("oracle backward: out of memory")
     return dh, dl, dg, dx
+
+
+def sign_grads(x, dy, bits_u, bits_v, h, l, g, gu0=None, gv0=None, accumulate: bool = False):
+    """Returns (G_U [d_out][r], G_V [d_in][r]) in f64: the gradients of
+    sum(dy * y) with respect to the entries of S_U and S_V taken as real
+    numbers. Without accumulate they are overwritten, else added to gu0/gv0."""
+    x, dy = _f64(x), _f64(dy)
+    M, d_in = x.shape
+    h, l, g = _f64(h), _f64(l), _f64(g)
+    d_out, r = h.size, l.size
+    assert dy.shape == (M, d_out) and g.size == d_in
+    bits_u, bits_v = _u32(bits_u), _u32(bits_v)
+    W = (r + 31) // 32
+    assert bits_u.size == d_out * W and bits_v.size == d_in * W
+    gu = np.zeros((d_out, r)) if gu0 is None else _f64(gu0).copy()
+    gv = np.zeros((d_in, r)) if gv0 is None else _f64(gv0).copy()
+    rc = _load().oracle_blr_sign_grads(M, d_in, d_out, r, _ptr(x), _ptr(dy), _ptr(bits_u), _ptr(bits_v), _ptr(h),
+                                       _ptr(l), _ptr(g), _ptr(gu), _ptr(gv), int(bool(accumulate)))
+    if rc != 0:
+        raise MemoryError("oracle sign gradients: out of memory")
+    return gu, gv
 
 
 def rel_frobenius(got, want) -> float:

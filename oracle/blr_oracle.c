@@ -197,3 +197,74 @@ int oracle_blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const
     free(DXP);
     return bad ? -1 : 0;
 }
+
+/* Sign gradients (page: `blr_backward` with sign state, and the f64 host
+ * reference `host_sign_grads` of its tests): the gradients of
+ * L = sum_{t,i} dy[t][i] y[t][i] with respect to the entries of S_U and S_V
+ * taken as real numbers,
+ *   a[t][k] = sum_j x[t][j] g[j] S_V[j][k]
+ *   b[t][k] = sum_i dy[t][i] h[i] S_U[i][k]
+ *   G_U[i][k] = (accumulate ? G_U[i][k] : 0) + h[i] l[k] sum_t dy[t][i] a[t][k]
+ *   G_V[j][k] = (accumulate ? G_V[j][k] : 0) + g[j] l[k] sum_t x[t][j] b[t][k]
+ * The per-token arrays a and b are formed first (in parallel over tokens),
+ * then each row of G sums over the tokens in order (in parallel over rows).
+ * Returns 0, or -1 when memory runs out. */
+int oracle_blr_sign_grads(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const double *x, const double *dy,
+                          const uint32_t *bits_u, const uint32_t *bits_v, const double *h, const double *l,
+                          const double *g, double *gu, double *gv, int accumulate) {
+    double *SU = decode_alloc(bits_u, d_out, r);
+    double *SV = decode_alloc(bits_v, d_in, r);
+    double *A = (double *)malloc((size_t)(M * r) * sizeof(double));
+    double *B = (double *)malloc((size_t)(M * r) * sizeof(double));
+    int bad = (SU == NULL || SV == NULL || A == NULL || B == NULL);
+    if (!bad) {
+#pragma omp parallel for schedule(static)
+        for (int64_t t = 0; t < M; ++t) {
+            const double *xt = x + t * d_in, *dyt = dy + t * d_out;
+            double *a = A + t * r, *b = B + t * r;
+            for (int64_t k = 0; k < r; ++k) a[k] = b[k] = 0.0;
+            for (int64_t j = 0; j < d_in; ++j) {
+                const double xg = xt[j] * g[j];
+                const double *sv = SV + j * r;
+                for (int64_t k = 0; k < r; ++k) a[k] += xg * sv[k];
+            }
+            for (int64_t i = 0; i < d_out; ++i) {
+                const double dyh = dyt[i] * h[i];
+                const double *su = SU + i * r;
+                for (int64_t k = 0; k < r; ++k) b[k] += dyh * su[k];
+            }
+        }
+        /* G_U rows then G_V rows: out[row][k] = s[row] l[k] sum_t P[t][row] Q[t][k] */
+#pragma omp parallel
+        {
+            double *acc = (double *)malloc((size_t)r * sizeof(double));
+            if (acc == NULL) {
+#pragma omp atomic write
+                bad = 1;
+            } else {
+#pragma omp for schedule(static)
+                for (int64_t row = 0; row < d_out + d_in; ++row) {
+                    const int u = row < d_out;
+                    const int64_t i = u ? row : row - d_out;
+                    const int64_t n = u ? d_out : d_in;
+                    const double *P = u ? dy : x, *Q = u ? A : B;
+                    double *out = (u ? gu : gv) + i * r;
+                    const double s = u ? h[i] : g[i];
+                    for (int64_t k = 0; k < r; ++k) acc[k] = 0.0;
+                    for (int64_t t = 0; t < M; ++t) {
+                        const double p = P[t * n + i];
+                        const double *q = Q + t * r;
+                        for (int64_t k = 0; k < r; ++k) acc[k] += p * q[k];
+                    }
+                    for (int64_t k = 0; k < r; ++k) out[k] = (accumulate ? out[k] : 0.0) + s * l[k] * acc[k];
+                }
+            }
+            free(acc);
+        }
+    }
+    free(SU);
+    free(SV);
+    free(A);
+    free(B);
+    return bad ? -1 : 0;
+}

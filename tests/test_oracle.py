@@ -334,3 +334,98 @@ def test_workloads_shapes_and_scales():
     assert np.all((t["h"] >= 0.5) & (t["h"] <= 1.5)) and np.all((t["l"] >= 0) & (t["l"] <= 0.1))
     # same seed, same numbers
     assert np.array_equal(t["x"], synth.inputs(synth.WORKLOADS[synth.SMALL])["x"])
+
+
+# ------------------------------------------------------- sign gradients --
+
+def _relaxed_loss(p, dy, SU, SV):
+    """sum(dy * y) with the sign matrices taken as real matrices (dense)."""
+    x, h, l, g = (p[k].astype(np.float64) for k in ("x", "h", "l", "g"))
+    W = (h[:, None] * SU) @ (l[:, None] * SV.T) * g[None, :]
+    return float(np.sum(dy * (x @ W.T)))
+
+
+def test_sign_grads_match_relaxed_central_differences():
+    """G_U and G_V are the gradients of L = sum(dy * y) with respect to the
+    entries of S_U and S_V taken as real numbers; L is linear in each entry,
+    so the central difference quotient of the dense form is exact."""
+    M, d_in, d_out, r = 6, 10, 9, 40
+    p = small(M, d_in, d_out, r, seed=81)
+    dy = p["dy"].astype(np.float64)
+    SU = unpack_signs(p["bits_u"], d_out, r)
+    SV = unpack_signs(p["bits_v"], d_in, r)
+    GU, GV = oracle.sign_grads(p["x"], p["dy"], p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"])
+    eps = 0.25
+    fd_u = np.empty_like(GU)
+    for i in range(d_out):
+        for k in range(r):
+            E = np.zeros_like(SU)
+            E[i, k] = eps
+            fd_u[i, k] = (_relaxed_loss(p, dy, SU + E, SV) - _relaxed_loss(p, dy, SU - E, SV)) / (2 * eps)
+    fd_v = np.empty_like(GV)
+    for j in range(d_in):
+        for k in range(r):
+            E = np.zeros_like(SV)
+            E[j, k] = eps
+            fd_v[j, k] = (_relaxed_loss(p, dy, SU, SV + E) - _relaxed_loss(p, dy, SU, SV - E)) / (2 * eps)
+    assert oracle.rel_frobenius(GU, fd_u) < 1e-12
+    assert oracle.rel_frobenius(GV, fd_v) < 1e-12
+
+
+def test_sign_grads_flip_identity():
+    """The page's flip identity with the oracle's G_U, G_V: flipping one bit
+    and rerunning the oracle forward changes L = 1/2 ||y - y*||^2 by exactly
+    -2 s G + (the quadratic term), at word-edge ranks."""
+    M, d_in, d_out, r = 16, 40, 36, 128
+    p = synth.exact_grid(M, d_in, d_out, r, 33)
+    x, h, l, g = (p[k].astype(np.float64) for k in ("x", "h", "l", "g"))
+    y0, a, _ = oracle.forward(p["x"], p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"])
+    ystar = y0 + 0.5 * np.sqrt(np.mean(y0 ** 2)) * np.random.default_rng(83).standard_normal(y0.shape)
+    dy = y0 - ystar
+    GU, GV = oracle.sign_grads(p["x"], dy, p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"])
+    SU = unpack_signs(p["bits_u"], d_out, r)
+    SV = unpack_signs(p["bits_v"], d_in, r)
+    L0 = 0.5 * np.sum(dy ** 2)
+    worst = 0.0
+    for side in ("U", "V"):
+        for (i, k) in [(0, 0), (3, 31), (7, 32), (35, 127), (11, 63), (20, 64), (2, 95), (9, 96)]:
+            bu, bv = p["bits_u"].copy(), p["bits_v"].copy()
+            if side == "U":
+                bu[i, k // 32] ^= np.uint32(1 << (k % 32))
+                quad = 2 * h[i] ** 2 * l[k] ** 2 * np.sum(a[:, k] ** 2)
+                pred, scale = -2 * SU[i, k] * GU[i, k] + quad, 2 * abs(GU[i, k]) + quad
+            else:
+                bv[i, k // 32] ^= np.uint32(1 << (k % 32))
+                quad = 2 * g[i] ** 2 * l[k] ** 2 * np.sum(x[:, i] ** 2) * np.sum(h ** 2)
+                pred, scale = -2 * SV[i, k] * GV[i, k] + quad, 2 * abs(GV[i, k]) + quad
+            y1, _, _ = oracle.forward(p["x"], bu, bv, p["h"], p["l"], p["g"], tape=False)
+            worst = max(worst, abs(0.5 * np.sum((y1 - ystar) ** 2) - L0 - pred) / scale)
+    assert worst < 1e-9
+
+
+def test_sign_grads_euler_identities_against_the_backward():
+    """sum_k S_U[i][k] G_U[i][k] = h_i dh_i and sum_k S_V[j][k] G_V[j][k] =
+    g_j dg_j (y is linear in S_U and in S_V, so scaling a row of S scales the
+    row's outputs; dh and dg come from the separately pinned backward)."""
+    M, d_in, d_out, r = 23, 70, 50, 96
+    p = small(M, d_in, d_out, r, seed=85)
+    GU, GV = oracle.sign_grads(p["x"], p["dy"], p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"])
+    dh, _, dg, _ = oracle.backward(p["x"], p["dy"], p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"])
+    SU = unpack_signs(p["bits_u"], d_out, r)
+    SV = unpack_signs(p["bits_v"], d_in, r)
+    h, g = p["h"].astype(np.float64), p["g"].astype(np.float64)
+    assert oracle.rel_frobenius(np.sum(SU * GU, axis=1), h * dh) < 1e-12
+    assert oracle.rel_frobenius(np.sum(SV * GV, axis=1), g * dg) < 1e-12
+
+
+def test_sign_grads_accumulate_and_zero_dy():
+    M, d_in, d_out, r = 9, 20, 12, 64
+    p = small(M, d_in, d_out, r, seed=87)
+    GU, GV = oracle.sign_grads(p["x"], p["dy"], p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"])
+    rng = np.random.default_rng(3)
+    gu0, gv0 = rng.standard_normal(GU.shape), rng.standard_normal(GV.shape)
+    GU2, GV2 = oracle.sign_grads(p["x"], p["dy"], p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"],
+                                 gu0=gu0, gv0=gv0, accumulate=True)
+    assert np.allclose(GU2, gu0 + GU, rtol=0, atol=1e-13) and np.allclose(GV2, gv0 + GV, rtol=0, atol=1e-13)
+    Z = oracle.sign_grads(p["x"], np.zeros_like(p["dy"]), p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"])
+    assert not np.any(Z[0]) and not np.any(Z[1])
