@@ -7,7 +7,8 @@ There is no fallback: if the library is missing or the device is not
 gfx950, the calls raise.
 
 The functions carry the C names: `blr_expand_signs`, `blr_forward`,
-`blr_backward`, `blr_workspace_bytes`, plus the profiling calls.
+`blr_backward`, `blr_backward_signs`, `blr_workspace_bytes`, plus the
+profiling calls.
 """
 from __future__ import annotations
 
@@ -46,6 +47,9 @@ def load():
     lib.blr_forward.restype = i32
     lib.blr_backward.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, f32, p, p, p, p, i32, p, sz, p]
     lib.blr_backward.restype = i32
+    lib.blr_backward_signs.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, f32, p, p, p, p, i32, p, p, i32,
+                                       p, sz, p]
+    lib.blr_backward_signs.restype = i32
     lib.blr_profile_enable.argtypes = [i32]
     lib.blr_profile_enable.restype = i32
     lib.blr_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
@@ -192,6 +196,43 @@ def blr_backward(x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale: float, 
                                _ptr(dg), _ptr(dx), int(bool(accumulate_dx)), _ptr(ws), ws.numel(), _stream(stream)),
            "blr_backward")
     return dh, dl, dg, dx
+
+
+def blr_backward_signs(x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale: float, *, dh=None, dl=None, dg=None,
+                       dx=None, accumulate_dx=False, grad_u=None, grad_v=None, accumulate_signs=False, ws=None,
+                       stream=None):
+    """blr_backward plus the sign gradients G_U [d_out][r] and G_V [d_in][r]
+    (allocated when not given; overwritten unless accumulate_signs).
+    Returns (dh, dl, dg, dx, grad_u, grad_v)."""
+    import torch
+    f32 = (torch.float32,)
+    M, d_in = _need(x, "x", f32).shape
+    d_out, r = _need(h, "h", f32).shape[0], _need(l, "l", f32).shape[0]
+    _need(g, "g", f32, (d_in,))
+    _need(dy, "dy", f32, (M, d_out))
+    W = (r + 31) // 32
+    _need(bits_u, "bits_u", _bits_dtypes(), (d_out, W))
+    _need(bits_v, "bits_v", _bits_dtypes(), (d_in, W))
+    _need(tape_a, "tape_a", f32, (M, r))
+    if tape_c is not None:
+        _need(tape_c, "tape_c", f32, (M, d_out))
+    dev = x.device
+    dh = torch.zeros(d_out, dtype=torch.float32, device=dev) if dh is None else _need(dh, "dh", f32, (d_out,))
+    dl = torch.zeros(r, dtype=torch.float32, device=dev) if dl is None else _need(dl, "dl", f32, (r,))
+    dg = torch.zeros(d_in, dtype=torch.float32, device=dev) if dg is None else _need(dg, "dg", f32, (d_in,))
+    dx = torch.empty((M, d_in), dtype=torch.float32, device=dev) if dx is None else _need(dx, "dx", f32, (M, d_in))
+    grad_u = torch.empty((d_out, r), dtype=torch.float32, device=dev) if grad_u is None else \
+        _need(grad_u, "grad_u", f32, (d_out, r))
+    grad_v = torch.empty((d_in, r), dtype=torch.float32, device=dev) if grad_v is None else \
+        _need(grad_v, "grad_v", f32, (d_in, r))
+    if ws is None:
+        ws = workspace(M, d_in, d_out, r, dev)
+    _check(load().blr_backward_signs(M, d_in, d_out, r, _ptr(x), _ptr(dy), _ptr(bits_u), _ptr(bits_v), _ptr(h),
+                                     _ptr(l), _ptr(g), _ptr(tape_a), _ptr(tape_c), ctypes.c_float(gscale), _ptr(dh),
+                                     _ptr(dl), _ptr(dg), _ptr(dx), int(bool(accumulate_dx)), _ptr(grad_u),
+                                     _ptr(grad_v), int(bool(accumulate_signs)), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "blr_backward_signs")
+    return dh, dl, dg, dx, grad_u, grad_v
 
 
 def blr_profile_enable(max_launches: int):

@@ -226,12 +226,17 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
     return BLR_OK;
 }
 
-int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
-                 const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
-                 const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl, float *dg, float *dx,
-                 int accumulate_dx, void *workspace, size_t workspace_bytes, void *stream) {
+// The backward, and with grad_u / grad_v the sign gradients after it (both
+// or neither).
+static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
+                         const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                         const float *g, const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl,
+                         float *dg, float *dx, int accumulate_dx, float *grad_u, float *grad_v, int accumulate_signs,
+                         void *workspace, size_t workspace_bytes, void *stream) {
     if (!x || !dy || !bits_u || !bits_v || !h || !l || !g || !tape_a || !dh || !dl || !dg || !dx)
         return BLR_ERR_NULL;
+    if ((grad_u == nullptr) != (grad_v == nullptr)) return BLR_ERR_NULL;
+    if (grad_u && (!aligned16(grad_u) || !aligned16(grad_v))) return BLR_ERR_ALIGN;
     if (!shape_ok(M, d_in, d_out, r)) return BLR_ERR_SHAPE;
     if (!pow2_scale_ok(gscale)) return BLR_ERR_SCALE;
     const Layout L = layout(M, d_in, d_out, r);
@@ -333,7 +338,36 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
     fin.job[2] = {part_g, mt_b2, (int)d_in, dg};
     fin.count = 3;
     BLR_TRY(launch_finish(fin, s));
+
+    if (grad_u) {
+        // G_U = diag(h) dy^T a diag(l) from f16(dy.h.gs) and f16(a.l);
+        // G_V = diag(g) x^T db diag(l) from f16(x.g) and f16(db.l.gs); both / gs
+        TnJobs tj = {};
+        tj.T = M;
+        tj.count = 2;
+        tj.job[0] = {dy, h, gscale, tape_a, l, 1.0f, (int)d_out, (int)r, inv, grad_u, accumulate_signs ? 1 : 0, 0};
+        tj.job[1] = {x, g, 1.0f, db, l, gscale, (int)d_in, (int)r, inv, grad_v, accumulate_signs ? 1 : 0, 0};
+        BLR_TRY(launch_gemm_tn(tj, s));
+    }
     return BLR_OK;
+}
+
+int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
+                 const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                 const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl, float *dg, float *dx,
+                 int accumulate_dx, void *workspace, size_t workspace_bytes, void *stream) {
+    return backward_impl(M, d_in, d_out, r, x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale, dh, dl, dg, dx,
+                         accumulate_dx, nullptr, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
+                       const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                       const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl, float *dg,
+                       float *dx, int accumulate_dx, float *grad_u, float *grad_v, int accumulate_signs,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    if (!grad_u || !grad_v) return BLR_ERR_NULL;
+    return backward_impl(M, d_in, d_out, r, x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale, dh, dl, dg, dx,
+                         accumulate_dx, grad_u, grad_v, accumulate_signs, workspace, workspace_bytes, stream);
 }
 
 int blr_profile_enable(int max_launches) {

@@ -30,6 +30,7 @@ enum KernelId {
     K_GEMM_DH,   // c recomputed as in F2, partials of dh = sum_t dy.c
     K_FINISH,    // sum of partials into dh / dl / dg
     K_GEMM_B1_DH, // B1 with dh fused (c recomputed per column block)
+    K_GEMM_SIGNS, // sign gradients G_U, G_V (contractions over tokens)
     K_COUNT
 };
 const char *kernel_name(int id);
@@ -92,7 +93,30 @@ struct FinishJobs {
     int count;
 };
 
+// Token-contraction jobs for the sign gradients:
+//   out[m][n] (+)= (sum_t f16(A[t][m] acol[m] ascale) f16(B[t][n] bcol[n] bscale)) oscale
+// A [T][Mo] and B [T][No] row-major; out [Mo][No]; Mo, No multiples of 128.
+struct TnJob {
+    const float *A;
+    const float *acol;
+    float ascale;
+    const float *B;
+    const float *bcol;
+    float bscale;
+    int Mo, No;
+    float oscale;
+    float *out;
+    int acc;
+    int tiles_before;  // filled by the launcher
+};
+struct TnJobs {
+    TnJob job[2];
+    int count;
+    int64_t T;
+};
+
 // Launchers: enqueue on `s`, return the launch error (hipSuccess if none).
+hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s);
 hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s);
 // out [r][rows/32]: bit (i % 32) of word i / 32 in row k is rank k of row i
 // of bits [rows][r/32] (rows and r multiples of 32).

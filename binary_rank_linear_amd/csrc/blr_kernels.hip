@@ -700,6 +700,132 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Sign gradients (page: `blr_backward` with sign state, `cvt_t` staging):
+// contractions over the tokens of two [T][*] activations,
+//   out[m][n] (+)= (sum_t f16(A[t][m] acol[m] ascale) f16(B[t][n] bcol[n] bscale)) oscale.
+// Per step of 32 tokens each thread loads a 4-token x 4-column block of A
+// and of B (a wave's loads cover 8 rows x 128 bytes), scales and rounds it
+// to f16 and writes it transposed ([column][token]) into LDS, so both MFMA
+// operands read 8 consecutive tokens per lane; two LDS buffers, the next
+// step's loads in flight during the MFMAs. Tokens past T are zero. 128x128
+// tiles of 2x2 waves; one launch serves both gradients.
+constexpr int TN_BM = 128, TN_BN = 128, TN_LDK = 40;
+__global__ __launch_bounds__(256) void gemm_tn_kernel(TnJobs jobs) {
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][TN_BM * TN_LDK];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TN_BN * TN_LDK];
+    int b = blockIdx.x, j = 0;
+    if (jobs.count > 1 && b >= jobs.job[1].tiles_before) j = 1;
+    const TnJob &jb = jobs.job[j];
+    b -= jb.tiles_before;
+    const int ntn = jb.No / TN_BN;
+    const int mt = b / ntn, nt = b - mt * ntn;
+    const int m0 = mt * TN_BM, n0 = nt * TN_BN;
+    const int64_t T = jobs.T;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    // staging block of this thread: tokens 4*tb .. +3 of the step, columns
+    // 4*cb .. +3 of the tile
+    const int tb = lane & 7, cb = wave * 8 + (lane >> 3);
+    f32x4_t as, bs;  // column scales of the thread's 4 columns
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        as[e] = jb.acol[m0 + 4 * cb + e] * jb.ascale;
+        bs[e] = jb.bcol[n0 + 4 * cb + e] * jb.bscale;
+    }
+    const float *Ab = jb.A + m0 + 4 * cb;
+    const float *Bb = jb.B + n0 + 4 * cb;
+    const int64_t nk = (T + 31) / 32;
+    f32x4_t ra[4], rb[4];
+#define TN_LOAD(kt)                                                                        \
+    do {                                                                                   \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
+            const int64_t t_ = (int64_t)(kt) * 32 + 4 * tb + e;                            \
+            const int64_t tc_ = t_ < T ? t_ : T - 1;                                       \
+            f32x4_t va_ = *reinterpret_cast<const f32x4_t *>(Ab + tc_ * jb.Mo);            \
+            f32x4_t vb_ = *reinterpret_cast<const f32x4_t *>(Bb + tc_ * jb.No);            \
+            const f32x4_t z_ = {0.f, 0.f, 0.f, 0.f};                                       \
+            ra[e] = t_ < T ? va_ : z_;                                                     \
+            rb[e] = t_ < T ? vb_ : z_;                                                     \
+        }                                                                                  \
+    } while (0)
+#define TN_STORE(buf)                                                                      \
+    do {                                                                                   \
+        _Pragma("unroll") for (int c_ = 0; c_ < 4; ++c_) {                                 \
+            uint2 ha_, hb_;                                                                \
+            ha_.x = f16x2_scaled(ra[0][c_], as[c_], ra[1][c_], as[c_]);                    \
+            ha_.y = f16x2_scaled(ra[2][c_], as[c_], ra[3][c_], as[c_]);                    \
+            hb_.x = f16x2_scaled(rb[0][c_], bs[c_], rb[1][c_], bs[c_]);                    \
+            hb_.y = f16x2_scaled(rb[2][c_], bs[c_], rb[3][c_], bs[c_]);                    \
+            *reinterpret_cast<uint2 *>(&As[buf][(4 * cb + c_) * TN_LDK + 4 * tb]) = ha_;  \
+            *reinterpret_cast<uint2 *>(&Bs[buf][(4 * cb + c_) * TN_LDK + 4 * tb]) = hb_;  \
+        }                                                                                  \
+    } while (0)
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
+    TN_LOAD(0);
+    TN_STORE(0);
+    __syncthreads();
+    const int aro = (wm * 64 + (lane & 31)) * TN_LDK + (lane >> 5) * 8;
+    const int bro = (wn * 64 + (lane & 31)) * TN_LDK + (lane >> 5) * 8;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = (int)(kt & 1);
+        TN_LOAD(kt + 1 < nk ? kt + 1 : kt);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            half8_t fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                fa[i] = *reinterpret_cast<const half8_t *>(&As[cur][aro + i * 32 * TN_LDK + s * 16]);
+                fb[i] = *reinterpret_cast<const half8_t *>(&Bs[cur][bro + i * 32 * TN_LDK + s * 16]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+        }
+        TN_STORE(cur ^ 1);
+        __syncthreads();
+    }
+#undef TN_LOAD
+#undef TN_STORE
+    // out rows m0 + wm*64 + i*32 + 8*(v/4) + 4*(lane/32) + v%4, columns
+    // n0 + wn*64 + jj*32 + lane%32
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            float *o = jb.out + row * jb.No + n0 + wn * 64 + (lane & 31);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const float val = acc[i][jj][v] * jb.oscale;
+                o[jj * 32] = jb.acc ? o[jj * 32] + val : val;
+            }
+        }
+}
+
+hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
+    int total = 0;
+    for (int j = 0; j < jobs.count; ++j) {
+        if (jobs.job[j].Mo % TN_BM || jobs.job[j].No % TN_BN || jobs.T < 1) return hipErrorInvalidValue;
+        jobs.job[j].tiles_before = total;
+        total += (jobs.job[j].Mo / TN_BM) * (jobs.job[j].No / TN_BN);
+    }
+    prof_begin(K_GEMM_SIGNS, s);
+    hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)total), dim3(256), 0, s, jobs);
+    hipError_t e = hipGetLastError();
+    prof_end(s);
+    return e;
+}
+
+// ---------------------------------------------------------------------------
 // Column reduction (page: `colsum_prod`, one thread per column with a serial
 // row loop, later two-pass): here each thread owns 4 adjacent columns
 // (float4, so a wavefront reads 1 KB contiguous per row) over COLSUM_ROWS
@@ -800,6 +926,7 @@ const char *kernel_name(int id) {
         case K_GEMM_DH: return "gemm_dh_recompute_c";
         case K_FINISH: return "colsum_finish";
         case K_GEMM_B1_DH: return "gemm_b1_dh_fused";
+        case K_GEMM_SIGNS: return "gemm_sign_grads";
     }
     return "?";
 }

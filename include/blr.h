@@ -122,6 +122,25 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
                  int accumulate_dx, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Backward with the sign gradients (page: `blr_backward` with sign state;
+ * the f64 host reference of its tests): blr_backward, then
+ *   grad_u [d_out][r]: G_U = diag(h) . dy^T . a . diag(l)
+ *   grad_v [d_in][r]:  G_V = diag(g) . x^T . db . diag(l),  db = (dy.h) S_U
+ * the gradients of sum(dy.y) with respect to the entries of S_U and S_V
+ * taken as real numbers (what a sign update consumes). As on the page both
+ * are contractions over the tokens of f16-staged operands with f32
+ * accumulation: f16(dy.h.gscale) with f16(a.l), and f16(x.g) with
+ * f16(db.l.gscale), each product divided by gscale. accumulate_signs = 0
+ * overwrites grad_u / grad_v, 1 adds. Every other argument, rule and error
+ * is blr_backward's; grad_u and grad_v must be non-NULL and 16-byte aligned.
+ */
+int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
+                       const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                       const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl, float *dg,
+                       float *dx, int accumulate_dx, float *grad_u, float *grad_v, int accumulate_signs,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Per-kernel timing with HIP events (the role of the page's trainer
  * profiling marks). blr_profile_enable(n) creates a pool of event pairs for
  * up to n launches and brackets every later launch of this library with a

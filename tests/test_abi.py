@@ -169,3 +169,28 @@ def test_expand_rejects_bad_arguments(ptrs):
     assert lib.blr_expand_signs(f(), 0, 32, f(), None, None) == E_SHAPE
     assert lib.blr_expand_signs(f(), 4, 0, None, f(), None) == E_SHAPE
     assert lib.blr_expand_signs(f(), 4, 32, f(offset=2), None, None) == E_ALIGN
+
+
+def bwd_signs(lib, M, d_in, d_out, r, ptrs, gscale=1024.0):
+    ws_bytes = blr.blr_workspace_bytes(M, d_in, d_out, r)
+    return lib.blr_backward_signs(M, d_in, d_out, r, ptrs["x"], ptrs["dy"], ptrs["bu"], ptrs["bv"], ptrs["h"],
+                                  ptrs["l"], ptrs["g"], ptrs["ta"], ptrs["tc"], ctypes.c_float(gscale), ptrs["dh"],
+                                  ptrs["dl"], ptrs["dg"], ptrs["dx"], 0, ptrs["gu"], ptrs["gv"], 0, ptrs["ws"],
+                                  ws_bytes, None)
+
+
+def test_backward_signs_rejects_bad_arguments(ptrs):
+    lib = blr.load()
+    f = ptrs["_fake"]
+    p = dict(ptrs)
+    p["gu"], p["gv"] = f(), f()
+    for k in ["gu", "gv", "x", "dy", "ta"]:
+        q = dict(p)
+        q[k] = None
+        assert bwd_signs(lib, 128, 256, 256, 128, q) == E_NULL, k
+    for k in ["gu", "gv"]:
+        q = dict(p)
+        q[k] = f(offset=4)
+        assert bwd_signs(lib, 128, 256, 256, 128, q) == E_ALIGN, k
+    assert bwd_signs(lib, 128, 200, 256, 128, p) == E_SHAPE
+    assert bwd_signs(lib, 128, 256, 256, 128, p, gscale=3.0) == E_SCALE
