@@ -51,6 +51,8 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
         return M * (do + 2 * r) * f32 + 2 * r * do / 8 + do * f32 + r * f32, 4.0 * M * r * do
     if name == "gemm_b2_dbl_svt":    # read db and x, write dx
         return M * (r + 2 * di) * f32 + di * r / 8 + (r + di) * f32, 2.0 * M * di * r
+    if name == "gemm_sign_grads":    # read dy, a, x, db; write G_U, G_V
+        return M * (do + di + 2 * r) * f32 + (do + di) * r * f32, 2.0 * M * r * (do + di)
     if name == "colsum_dy_c":        # read dy and c
         return 2.0 * M * do * f32, 2.0 * M * do
     if name == "transpose_bits":     # one bitmap in, its transpose out (average of U and V)
@@ -243,6 +245,27 @@ def main():
     roof["kernel"] = dom
     roof["avg_us"] = round(avg_s * 1e6, 3)
 
+    # sign gradients (blr_backward_signs, not part of the headline step):
+    # the duration of their contraction over the same K backward calls
+    gu = torch.empty((do, r), dtype=torch.float32, device=dev)
+    gv = torch.empty((di, r), dtype=torch.float32, device=dev)
+    blr.blr_profile_enable(args.steps * 16)
+    blr.blr_profile_reset()
+    for _ in range(args.steps):
+        blr.blr_backward_signs(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc, w.gscale,
+                               dh=dh, dl=dl, dg=dg, dx=dx, grad_u=gu, grad_v=gv, ws=ws)
+    torch.cuda.synchronize()
+    sprof = blr.blr_profile_read()
+    blr.blr_profile_enable(0)
+    sign = None
+    if "gemm_sign_grads" in sprof:
+        cnt, tot = sprof["gemm_sign_grads"]
+        s_us = 1000.0 * tot / cnt
+        sb, sf = kernel_work("gemm_sign_grads", w)
+        sign = {"avg_us": round(s_us, 3), "tflops": round(sf / (s_us * 1e-6) / 1e12, 1),
+                "frac_f16_peak": round(sf / (s_us * 1e-6) / 1e12 / PEAK_F16_TFLOPS, 4),
+                "gbs": round(sb / (s_us * 1e-6) / 1e9, 1)}
+
     tokens_s = M / (ms / 1000.0)
     tf_metric = w.flops_metric() / (ms / 1000.0) / 1e12
     tf_mfma = w.flops_mfma() / (ms / 1000.0) / 1e12
@@ -269,6 +292,7 @@ def main():
         "bwd_ms": round(bwd_ms, 5),
         "kernels": kernels,
         "roofline": roof,
+        "sign_grads": sign,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

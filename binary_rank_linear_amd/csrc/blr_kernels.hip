@@ -703,14 +703,16 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
 // Sign gradients (page: `blr_backward` with sign state, `cvt_t` staging):
 // contractions over the tokens of two [T][*] activations,
 //   out[m][n] (+)= (sum_t f16(A[t][m] acol[m] ascale) f16(B[t][n] bcol[n] bscale)) oscale.
-// Per step of 32 tokens each thread loads a 4-token x 4-column block of A
-// and of B (a wave's loads cover 8 rows x 128 bytes), scales and rounds it
-// to f16 and writes it transposed ([column][token]) into LDS, so both MFMA
-// operands read 8 consecutive tokens per lane; two LDS buffers, the next
-// step's loads in flight during the MFMAs. Tokens past T are zero. 128x128
-// tiles of 2x2 waves; one launch serves both gradients.
+// 128x128 tiles, 8 waves. Per step of 32 tokens, waves 0-3 stage A and
+// waves 4-7 stage B: each thread loads a 4-token x 4-column block (a wave's
+// loads cover 8 rows x 128 bytes), scales and rounds it to f16 and writes it
+// transposed ([column][token]) into LDS, so both MFMA operands read 8
+// consecutive tokens per lane. A register ring keeps the loads TP - 1 steps
+// ahead; two LDS buffers; tokens past T are zero (only the last step checks).
+// The 8 waves multiply in a 4x2 layout of 32x64 blocks. One launch serves
+// both gradients.
 constexpr int TN_BM = 128, TN_BN = 128, TN_LDK = 40;
-__global__ __launch_bounds__(256) void gemm_tn_kernel(TnJobs jobs) {
+__global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
     __shared__ __attribute__((aligned(16))) _Float16 As[2][TN_BM * TN_LDK];
     __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TN_BN * TN_LDK];
     int b = blockIdx.x, j = 0;
@@ -723,92 +725,96 @@ __global__ __launch_bounds__(256) void gemm_tn_kernel(TnJobs jobs) {
     const int64_t T = jobs.T;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    // staging block of this thread: tokens 4*tb .. +3 of the step, columns
-    // 4*cb .. +3 of the tile
-    const int tb = lane & 7, cb = wave * 8 + (lane >> 3);
-    f32x4_t as, bs;  // column scales of the thread's 4 columns
+    const int wm = wave >> 1, wn = wave & 1;   // 32-row x 64-column MMA block
+    const bool bside = wave >= 4;              // stages B (else A)
+    // staging block: tokens 4*tb .. +3 of the step, columns 4*cb .. +3 of the tile
+    const int tb = lane & 7, cb = (wave & 3) * 8 + (lane >> 3);
+    const float *col = bside ? jb.bcol + n0 : jb.acol + m0;
+    const float sc = bside ? jb.bscale : jb.ascale;
+    f32x4_t cs;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        as[e] = jb.acol[m0 + 4 * cb + e] * jb.ascale;
-        bs[e] = jb.bcol[n0 + 4 * cb + e] * jb.bscale;
-    }
-    const float *Ab = jb.A + m0 + 4 * cb;
-    const float *Bb = jb.B + n0 + 4 * cb;
+    for (int e = 0; e < 4; ++e) cs[e] = col[4 * cb + e] * sc;
+    const int64_t ld = bside ? jb.No : jb.Mo;
+    const float *src = (bside ? jb.B + n0 : jb.A + m0) + 4 * cb;
+    _Float16 *dst0 = (bside ? &Bs[0][0] : &As[0][0]) + 4 * cb * TN_LDK + 4 * tb;
+    constexpr int BUFH = TN_BM * TN_LDK;  // halves per buffer (A and B alike)
     const int64_t nk = (T + 31) / 32;
-    f32x4_t ra[4], rb[4];
-#define TN_LOAD(kt)                                                                        \
+    constexpr int TP = 4;
+    f32x4_t rg[TP][4];
+#define TN_LOAD(q, kt)                                                                     \
     do {                                                                                   \
-        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
-            const int64_t t_ = (int64_t)(kt) * 32 + 4 * tb + e;                            \
-            const int64_t tc_ = t_ < T ? t_ : T - 1;                                       \
-            f32x4_t va_ = *reinterpret_cast<const f32x4_t *>(Ab + tc_ * jb.Mo);            \
-            f32x4_t vb_ = *reinterpret_cast<const f32x4_t *>(Bb + tc_ * jb.No);            \
-            const f32x4_t z_ = {0.f, 0.f, 0.f, 0.f};                                       \
-            ra[e] = t_ < T ? va_ : z_;                                                     \
-            rb[e] = t_ < T ? vb_ : z_;                                                     \
+        const int64_t k_ = (kt) < nk ? (kt) : nk - 1;                                      \
+        const int64_t t0_ = k_ * 32 + 4 * tb;                                              \
+        if (k_ * 32 + 32 <= T) {                                                           \
+            _Pragma("unroll") for (int e = 0; e < 4; ++e)                                  \
+                rg[q][e] = *reinterpret_cast<const f32x4_t *>(src + (t0_ + e) * ld);       \
+        } else {                                                                           \
+            _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                \
+                const int64_t tc_ = t0_ + e < T ? t0_ + e : T - 1;                         \
+                const f32x4_t v_ = *reinterpret_cast<const f32x4_t *>(src + tc_ * ld);     \
+                const f32x4_t z_ = {0.f, 0.f, 0.f, 0.f};                                   \
+                rg[q][e] = t0_ + e < T ? v_ : z_;                                          \
+            }                                                                              \
         }                                                                                  \
     } while (0)
-#define TN_STORE(buf)                                                                      \
+#define TN_STORE(q, buf)                                                                   \
     do {                                                                                   \
         _Pragma("unroll") for (int c_ = 0; c_ < 4; ++c_) {                                 \
-            uint2 ha_, hb_;                                                                \
-            ha_.x = f16x2_scaled(ra[0][c_], as[c_], ra[1][c_], as[c_]);                    \
-            ha_.y = f16x2_scaled(ra[2][c_], as[c_], ra[3][c_], as[c_]);                    \
-            hb_.x = f16x2_scaled(rb[0][c_], bs[c_], rb[1][c_], bs[c_]);                    \
-            hb_.y = f16x2_scaled(rb[2][c_], bs[c_], rb[3][c_], bs[c_]);                    \
-            *reinterpret_cast<uint2 *>(&As[buf][(4 * cb + c_) * TN_LDK + 4 * tb]) = ha_;  \
-            *reinterpret_cast<uint2 *>(&Bs[buf][(4 * cb + c_) * TN_LDK + 4 * tb]) = hb_;  \
+            uint2 h_;                                                                      \
+            h_.x = f16x2_scaled(rg[q][0][c_], cs[c_], rg[q][1][c_], cs[c_]);               \
+            h_.y = f16x2_scaled(rg[q][2][c_], cs[c_], rg[q][3][c_], cs[c_]);               \
+            *reinterpret_cast<uint2 *>(dst0 + (buf) * BUFH + c_ * TN_LDK) = h_;            \
         }                                                                                  \
     } while (0)
-    f32x16_t acc[2][2];
+    f32x16_t acc[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int v = 0; v < 16; ++v) acc[jj][v] = 0.0f;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
-    TN_LOAD(0);
-    TN_STORE(0);
+    for (int q = 0; q < TP; ++q) TN_LOAD(q, q);
+    TN_STORE(0, 0);
+    TN_LOAD(0, TP);
     __syncthreads();
-    const int aro = (wm * 64 + (lane & 31)) * TN_LDK + (lane >> 5) * 8;
+    const int aro = (wm * 32 + (lane & 31)) * TN_LDK + (lane >> 5) * 8;
     const int bro = (wn * 64 + (lane & 31)) * TN_LDK + (lane >> 5) * 8;
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        TN_LOAD(kt + 1 < nk ? kt + 1 : kt);
+    for (int64_t kt0 = 0; kt0 < nk; kt0 += TP) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            half8_t fa[2], fb[2];
+        for (int u = 0; u < TP; ++u) {
+            const int64_t kt = kt0 + u;
+            if (kt >= nk) break;  // uniform
+            const int cur = (int)(kt & 1);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                fa[i] = *reinterpret_cast<const half8_t *>(&As[cur][aro + i * 32 * TN_LDK + s * 16]);
-                fb[i] = *reinterpret_cast<const half8_t *>(&Bs[cur][bro + i * 32 * TN_LDK + s * 16]);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int s = 0; s < 2; ++s) {
+                const half8_t fa = *reinterpret_cast<const half8_t *>(&As[cur][aro + s * 16]);
+                half8_t fb[2];
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+                    fb[jj] = *reinterpret_cast<const half8_t *>(&Bs[cur][bro + jj * 32 * TN_LDK + s * 16]);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb[jj], acc[jj], 0, 0, 0);
+            }
+            TN_STORE((u + 1) % TP, cur ^ 1);
+            TN_LOAD((u + 1) % TP, kt + 1 + TP);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
         }
-        TN_STORE(cur ^ 1);
-        __syncthreads();
     }
 #undef TN_LOAD
 #undef TN_STORE
-    // out rows m0 + wm*64 + i*32 + 8*(v/4) + 4*(lane/32) + v%4, columns
+    // out rows m0 + wm*32 + 8*(v/4) + 4*(lane/32) + v%4, columns
     // n0 + wn*64 + jj*32 + lane%32
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        float *o = jb.out + row * jb.No + n0 + wn * 64 + (lane & 31);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            float *o = jb.out + row * jb.No + n0 + wn * 64 + (lane & 31);
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const float val = acc[i][jj][v] * jb.oscale;
-                o[jj * 32] = jb.acc ? o[jj * 32] + val : val;
-            }
+        for (int jj = 0; jj < 2; ++jj) {
+            const float val = acc[jj][v] * jb.oscale;
+            o[jj * 32] = jb.acc ? o[jj * 32] + val : val;
         }
+    }
 }
 
 hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
@@ -819,7 +825,7 @@ hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
         total += (jobs.job[j].Mo / TN_BM) * (jobs.job[j].No / TN_BN);
     }
     prof_begin(K_GEMM_SIGNS, s);
-    hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)total), dim3(256), 0, s, jobs);
+    hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)total), dim3(512), 0, s, jobs);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
