@@ -55,6 +55,8 @@ def _load():
         lib.oracle_blr_backward.restype = i32
         lib.oracle_blr_sign_grads.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, i32]
         lib.oracle_blr_sign_grads.restype = i32
+        lib.oracle_sumsq.argtypes = [p, i64]
+        lib.oracle_sumsq.restype = ctypes.c_double
         _lib = lib
     return _lib
 
@@ -160,6 +162,12 @@ def sign_grads(x, dy, bits_u, bits_v, h, l, g, gu0=None, gv0=None, accumulate: b
     if rc != 0:
         raise MemoryError("oracle sign gradients: out of memory")
     return gu, gv
+
+
+def sumsq(a) -> float:
+    """sum(a**2) in f64, in index order; non-finite values propagate."""
+    a = _f64(a).ravel()
+    return float(_load().oracle_sumsq(_ptr(a), a.size))
 
 
 def rel_frobenius(got, want) -> float:

@@ -268,3 +268,12 @@ int oracle_blr_sign_grads(int64_t M, int64_t d_in, int64_t d_out, int64_t r, con
     free(B);
     return bad ? -1 : 0;
 }
+
+/* Sum of squares (page: `sumsq` shader and wrapper, used to check a buffer
+ * for non-finite values): sum_i a[i]^2 in f64, in index order. Non-finite
+ * inputs propagate (inf or NaN result). */
+double oracle_sumsq(const double *a, int64_t n) {
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += a[i] * a[i];
+    return s;
+}

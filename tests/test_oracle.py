@@ -429,3 +429,17 @@ def test_sign_grads_accumulate_and_zero_dy():
     assert np.allclose(GU2, gu0 + GU, rtol=0, atol=1e-13) and np.allclose(GV2, gv0 + GV, rtol=0, atol=1e-13)
     Z = oracle.sign_grads(p["x"], np.zeros_like(p["dy"]), p["bits_u"], p["bits_v"], p["h"], p["l"], p["g"])
     assert not np.any(Z[0]) and not np.any(Z[1])
+
+
+# ----------------------------------------------------------- sum of squares --
+
+def test_sumsq_closed_forms_and_non_finite():
+    assert oracle.sumsq(np.array([3.0, 4.0])) == 25.0
+    assert oracle.sumsq(np.ones(1000)) == 1000.0
+    assert oracle.sumsq(np.zeros(7)) == 0.0
+    n = 1001
+    k = np.arange(1, n + 1, dtype=np.float64)
+    assert oracle.sumsq(k) == n * (n + 1) * (2 * n + 1) / 6  # exact in f64 at this size
+    assert oracle.sumsq(np.array([1.0, np.inf, 2.0])) == np.inf
+    assert np.isnan(oracle.sumsq(np.array([1.0, np.nan])))
+    assert np.isnan(oracle.sumsq(np.array([np.inf, -np.inf, np.nan])))
