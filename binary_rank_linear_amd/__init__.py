@@ -7,8 +7,9 @@ There is no fallback: if the library is missing or the device is not
 gfx950, the calls raise.
 
 The functions carry the C names: `blr_expand_signs`, `blr_forward`,
-`blr_backward`, `blr_backward_signs`, `blr_workspace_bytes`, plus the
-profiling calls.
+`blr_backward`, `blr_backward_signs`, `blr_sumsq`, `blr_workspace_bytes`,
+plus the profiling calls; `all_finite` and `next_gscale` are the host side
+of the finite check and the power-of-two loss scale.
 """
 from __future__ import annotations
 
@@ -50,6 +51,8 @@ def load():
     lib.blr_backward_signs.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, f32, p, p, p, p, i32, p, p, i32,
                                        p, sz, p]
     lib.blr_backward_signs.restype = i32
+    lib.blr_sumsq.argtypes = [p, i64, p, i32, p]
+    lib.blr_sumsq.restype = i32
     lib.blr_profile_enable.argtypes = [i32]
     lib.blr_profile_enable.restype = i32
     lib.blr_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
@@ -233,6 +236,31 @@ def blr_backward_signs(x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale: f
                                      _ptr(grad_v), int(bool(accumulate_signs)), _ptr(ws), ws.numel(),
                                      _stream(stream)), "blr_backward_signs")
     return dh, dl, dg, dx, grad_u, grad_v
+
+
+def blr_sumsq(a, nparts: int = 64, stream=None) -> float:
+    """Sum of squares of a float32 tensor: nparts device partials, added on
+    the host in f64 (the page's `sumsq`). Synchronises the stream."""
+    import torch
+    _need(a, "a", (torch.float32,))
+    parts = torch.empty(nparts, dtype=torch.float32, device=a.device)
+    _check(load().blr_sumsq(_ptr(a), a.numel(), _ptr(parts), int(nparts), _stream(stream)), "blr_sumsq")
+    return float(parts.double().sum().item())
+
+
+def all_finite(*tensors, stream=None) -> bool:
+    """True when every element of the float32 tensors is finite (each sum
+    of squares is finite; an overflowing square also reads as not finite)."""
+    import math
+    return all(math.isfinite(blr_sumsq(t, stream=stream)) for t in tensors)
+
+
+def next_gscale(gscale: float, finite: bool, lo: float = 1.0, hi: float = 2.0 ** 24) -> float:
+    """Power-of-two gradient staging scale for the next step: double it after
+    a step whose gradients were finite, halve it after one that overflowed,
+    within [lo, hi]."""
+    g = gscale * 2.0 if finite else gscale * 0.5
+    return min(max(g, lo), hi)
 
 
 def blr_profile_enable(max_launches: int):

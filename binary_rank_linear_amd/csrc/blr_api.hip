@@ -370,6 +370,16 @@ int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const 
                          accumulate_dx, grad_u, grad_v, accumulate_signs, workspace, workspace_bytes, stream);
 }
 
+int blr_sumsq(const float *a, int64_t n, float *partials, int nparts, void *stream) {
+    if (!a || !partials) return BLR_ERR_NULL;
+    if (n < 1 || nparts < 1 || nparts > 1024) return BLR_ERR_SHAPE;
+    if (!aligned16(a) || !aligned4(partials)) return BLR_ERR_ALIGN;
+    int st = current_device_ok();
+    if (st != BLR_OK) return st;
+    BLR_TRY(launch_sumsq(a, n, partials, nparts, (hipStream_t)stream));
+    return BLR_OK;
+}
+
 int blr_profile_enable(int max_launches) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     prof_release();

@@ -31,6 +31,7 @@ enum KernelId {
     K_FINISH,    // sum of partials into dh / dl / dg
     K_GEMM_B1_DH, // B1 with dh fused (c recomputed per column block)
     K_GEMM_SIGNS, // sign gradients G_U, G_V (contractions over tokens)
+    K_SUMSQ,      // sum-of-squares partials (finite check)
     K_COUNT
 };
 const char *kernel_name(int id);
@@ -117,6 +118,7 @@ struct TnJobs {
 
 // Launchers: enqueue on `s`, return the launch error (hipSuccess if none).
 hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s);
+hipError_t launch_sumsq(const float *a, int64_t n, float *partials, int nparts, hipStream_t s);
 hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s);
 // out [r][rows/32]: bit (i % 32) of word i / 32 in row k is rank k of row i
 // of bits [rows][r/32] (rows and r multiples of 32).

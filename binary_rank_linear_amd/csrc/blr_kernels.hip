@@ -832,6 +832,47 @@ hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Sum of squares (page: `sumsq` shader, the host's finite check): nparts
+// workgroups of 256 threads; thread t of workgroup p adds the squares of the
+// float4 groups p*256 + t + k*nparts*256 in order (workgroup 0 also takes the
+// n % 4 tail), then the 256 sums fold in a fixed tree. Non-finite values
+// propagate into the partial.
+__global__ __launch_bounds__(256) void sumsq_kernel(const float *__restrict__ a, int64_t n,
+                                                    float *__restrict__ partials) {
+    __shared__ float red[256];
+    const int t = threadIdx.x;
+    const int64_t n4 = n / 4;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    float acc = 0.0f;
+    for (int64_t c = (int64_t)blockIdx.x * 256 + t; c < n4; c += stride) {
+        const f32x4_t v = reinterpret_cast<const f32x4_t *>(a)[c];
+        acc += v.x * v.x;
+        acc += v.y * v.y;
+        acc += v.z * v.z;
+        acc += v.w * v.w;
+    }
+    if (blockIdx.x == 0 && t < n - n4 * 4) {
+        const float v = a[n4 * 4 + t];
+        acc += v * v;
+    }
+    red[t] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (t < w) red[t] = red[t] + red[t + w];
+        __syncthreads();
+    }
+    if (t == 0) partials[blockIdx.x] = red[0];
+}
+
+hipError_t launch_sumsq(const float *a, int64_t n, float *partials, int nparts, hipStream_t s) {
+    prof_begin(K_SUMSQ, s);
+    hipLaunchKernelGGL(sumsq_kernel, dim3((unsigned)nparts), dim3(256), 0, s, a, n, partials);
+    hipError_t e = hipGetLastError();
+    prof_end(s);
+    return e;
+}
+
+// ---------------------------------------------------------------------------
 // Column reduction (page: `colsum_prod`, one thread per column with a serial
 // row loop, later two-pass): here each thread owns 4 adjacent columns
 // (float4, so a wavefront reads 1 KB contiguous per row) over COLSUM_ROWS
@@ -933,6 +974,7 @@ const char *kernel_name(int id) {
         case K_FINISH: return "colsum_finish";
         case K_GEMM_B1_DH: return "gemm_b1_dh_fused";
         case K_GEMM_SIGNS: return "gemm_sign_grads";
+        case K_SUMSQ: return "sumsq";
     }
     return "?";
 }

@@ -141,6 +141,17 @@ int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const 
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Sum of squares (page: `sumsq` shader and wrapper, the host's check of a
+ * buffer for non-finite values): writes nparts f32 partial sums of a[i]^2,
+ * i < n, to the device array partials[nparts]; the caller adds them (the
+ * page adds them on the host in f64). A non-finite element makes its partial
+ * (and so the total) non-finite. Each partial covers a fixed set of elements
+ * summed in a fixed order: deterministic. 1 <= nparts <= 1024, n >= 1; a must
+ * be 16-byte aligned, partials 4-byte aligned.
+ */
+int blr_sumsq(const float *a, int64_t n, float *partials, int nparts, void *stream);
+
+/*
  * Per-kernel timing with HIP events (the role of the page's trainer
  * profiling marks). blr_profile_enable(n) creates a pool of event pairs for
  * up to n launches and brackets every later launch of this library with a

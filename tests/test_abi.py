@@ -194,3 +194,26 @@ def test_backward_signs_rejects_bad_arguments(ptrs):
         assert bwd_signs(lib, 128, 256, 256, 128, q) == E_ALIGN, k
     assert bwd_signs(lib, 128, 200, 256, 128, p) == E_SHAPE
     assert bwd_signs(lib, 128, 256, 256, 128, p, gscale=3.0) == E_SCALE
+
+
+def test_sumsq_rejects_bad_arguments(ptrs):
+    lib = blr.load()
+    f = ptrs["_fake"]
+    assert lib.blr_sumsq(None, 16, f(), 4, None) == E_NULL
+    assert lib.blr_sumsq(f(), 16, None, 4, None) == E_NULL
+    assert lib.blr_sumsq(f(), 0, f(), 4, None) == E_SHAPE
+    assert lib.blr_sumsq(f(), 16, f(), 0, None) == E_SHAPE
+    assert lib.blr_sumsq(f(), 16, f(), 1025, None) == E_SHAPE
+    assert lib.blr_sumsq(f(offset=4), 16, f(), 4, None) == E_ALIGN
+
+
+def test_next_gscale_doubles_on_success_and_halves_on_overflow():
+    assert blr.next_gscale(1024.0, True) == 2048.0
+    assert blr.next_gscale(1024.0, False) == 512.0
+    assert blr.next_gscale(2.0 ** 24, True) == 2.0 ** 24
+    assert blr.next_gscale(1.0, False) == 1.0
+    g = 2.0 ** 10
+    for finite in (True, False, False, True):
+        g = blr.next_gscale(g, finite)
+        m, e = np.frexp(g)
+        assert m == 0.5  # stays a power of two
