@@ -55,6 +55,9 @@ def _load():
         lib.oracle_blr_backward.restype = i32
         lib.oracle_blr_sign_grads.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, i32]
         lib.oracle_blr_sign_grads.restype = i32
+        lib.oracle_f16_decode.argtypes = [p, i64, p]
+        lib.oracle_plane_linear.argtypes = [i64, i64, i64, p, p, p]
+        lib.oracle_plane_linear.restype = i32
         lib.oracle_sumsq.argtypes = [p, i64]
         lib.oracle_sumsq.restype = ctypes.c_double
         _lib = lib
@@ -162,6 +165,28 @@ def sign_grads(x, dy, bits_u, bits_v, h, l, g, gu0=None, gv0=None, accumulate: b
     if rc != 0:
         raise MemoryError("oracle sign gradients: out of memory")
     return gu, gv
+
+
+def f16_decode(bits) -> np.ndarray:
+    """f64 values of IEEE binary16 bit patterns (uint16)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().oracle_f16_decode(_ptr(bits), bits.size, _ptr(out))
+    return out
+
+
+def plane_linear(x, plane_bits) -> np.ndarray:
+    """y [M][n] = x [M][k] times the transpose of the f16 plane [n][k] (uint16
+    bit patterns), in f64 (the page's `plane_linear`; its scale cancels)."""
+    x = _f64(x)
+    M, k = x.shape
+    plane_bits = np.ascontiguousarray(plane_bits, dtype=np.uint16)
+    n = plane_bits.shape[0]
+    assert plane_bits.shape == (n, k)
+    y = np.empty((M, n))
+    if _load().oracle_plane_linear(M, n, k, _ptr(x), _ptr(plane_bits), _ptr(y)) != 0:
+        raise MemoryError("oracle plane_linear: out of memory")
+    return y
 
 
 def sumsq(a) -> float:

@@ -21,6 +21,7 @@
  * token; over tokens in order for the column sums), so results do not
  * depend on the thread count.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -276,4 +277,36 @@ double oracle_sumsq(const double *a, int64_t n) {
     double s = 0.0;
     for (int64_t i = 0; i < n; ++i) s += a[i] * a[i];
     return s;
+}
+
+/* IEEE binary16 bit pattern -> double, exactly (sign, 5-bit exponent with
+ * bias 15, 10-bit fraction; subnormals, infinities and NaN included). */
+static double f16_to_f64(uint16_t hbits) {
+    const int sign = hbits >> 15, e = (hbits >> 10) & 31, f = hbits & 1023;
+    double v;
+    if (e == 0) v = (double)f / 1024.0 / 16384.0;                  /* f * 2^-24 */
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = (1.0 + (double)f / 1024.0) * ldexp(1.0, e - 15);
+    return sign ? -v : v;
+}
+
+void oracle_f16_decode(const uint16_t *h, int64_t n, double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_to_f64(h[i]);
+}
+
+/* Dense frozen linear (page: `plane_linear`): y[t][i] = sum_j x[t][j] P[i][j]
+ * with P the f16 plane [n][k] taken exactly; the staging scale cancels. */
+int oracle_plane_linear(int64_t M, int64_t n, int64_t k, const double *x, const uint16_t *plane, double *y) {
+    double *P = (double *)malloc((size_t)(n * k) * sizeof(double));
+    if (P == NULL) return -1;
+    oracle_f16_decode(plane, n * k, P);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < M; ++t)
+        for (int64_t i = 0; i < n; ++i) {
+            double s = 0.0;
+            for (int64_t j = 0; j < k; ++j) s += x[t * k + j] * P[i * k + j];
+            y[t * n + i] = s;
+        }
+    free(P);
+    return 0;
 }

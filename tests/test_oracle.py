@@ -443,3 +443,29 @@ def test_sumsq_closed_forms_and_non_finite():
     assert oracle.sumsq(np.array([1.0, np.inf, 2.0])) == np.inf
     assert np.isnan(oracle.sumsq(np.array([1.0, np.nan])))
     assert np.isnan(oracle.sumsq(np.array([np.inf, -np.inf, np.nan])))
+
+
+# ----------------------------------------------------------- plane_linear --
+
+def test_f16_decode_matches_numpy_float16():
+    pats = np.array([0x3C00, 0xBC00, 0x7BFF, 0x0001, 0x03FF, 0x0400, 0x8001, 0x0000, 0x8000, 0x7C00, 0xFC00,
+                     0x3555, 0x4248], dtype=np.uint16)
+    want = pats.view(np.float16).astype(np.float64)
+    got = oracle.f16_decode(pats)
+    assert np.array_equal(got, want)
+    assert np.isnan(oracle.f16_decode(np.array([0x7E00], np.uint16))[0])
+    allp = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    a, b = oracle.f16_decode(allp), allp.view(np.float16).astype(np.float64)
+    fin = np.isfinite(b)
+    assert np.array_equal(a[fin], b[fin]) and np.array_equal(np.isnan(a), np.isnan(b))
+
+
+def test_plane_linear_identity_and_dense():
+    rng = np.random.default_rng(91)
+    k = 48
+    x = rng.standard_normal((7, k))
+    eye = np.eye(k).astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.plane_linear(x, eye), x)
+    plane = rng.standard_normal((30, k)).astype(np.float16)
+    want = x @ plane.astype(np.float64).T
+    assert oracle.rel_frobenius(oracle.plane_linear(x, plane.view(np.uint16)), want) < 1e-14
