@@ -7,7 +7,7 @@ There is no fallback: if the library is missing or the device is not
 gfx950, the calls raise.
 
 The functions carry the C names: `blr_expand_signs`, `blr_forward`,
-`blr_backward`, `blr_backward_signs`, `blr_sumsq`, `blr_workspace_bytes`,
+`blr_backward`, `blr_backward_signs`, `blr_plane_linear`, `blr_sumsq`, `blr_workspace_bytes`,
 plus the profiling calls; `all_finite` and `next_gscale` are the host side
 of the finite check and the power-of-two loss scale.
 """
@@ -51,6 +51,8 @@ def load():
     lib.blr_backward_signs.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, f32, p, p, p, p, i32, p, p, i32,
                                        p, sz, p]
     lib.blr_backward_signs.restype = i32
+    lib.blr_plane_linear.argtypes = [i64, i64, i64, p, p, p, f32, p]
+    lib.blr_plane_linear.restype = i32
     lib.blr_sumsq.argtypes = [p, i64, p, i32, p]
     lib.blr_sumsq.restype = i32
     lib.blr_profile_enable.argtypes = [i32]
@@ -236,6 +238,20 @@ def blr_backward_signs(x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale: f
                                      _ptr(grad_v), int(bool(accumulate_signs)), _ptr(ws), ws.numel(),
                                      _stream(stream)), "blr_backward_signs")
     return dh, dl, dg, dx, grad_u, grad_v
+
+
+def blr_plane_linear(x, plane, scale: float = 1.0, *, y=None, stream=None):
+    """y [M][n] = (f16(x * scale) . plane^T) / scale with plane an f16 [n][k]
+    tensor (float16 or its int16 bit patterns). Returns y."""
+    import torch
+    M, k = _need(x, "x", (torch.float32,)).shape
+    n = _need(plane, "plane", (torch.float16, torch.int16)).shape[0]
+    _need(plane, "plane", (torch.float16, torch.int16), (n, k))
+    y = torch.empty((M, n), dtype=torch.float32, device=x.device) if y is None else \
+        _need(y, "y", (torch.float32,), (M, n))
+    _check(load().blr_plane_linear(M, n, k, _ptr(x), _ptr(plane), _ptr(y), ctypes.c_float(scale), _stream(stream)),
+           "blr_plane_linear")
+    return y
 
 
 def blr_sumsq(a, nparts: int = 64, stream=None) -> float:

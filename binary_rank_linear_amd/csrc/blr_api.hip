@@ -370,6 +370,31 @@ int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const 
                          accumulate_dx, grad_u, grad_v, accumulate_signs, workspace, workspace_bytes, stream);
 }
 
+int blr_plane_linear(int64_t M, int64_t n, int64_t k, const float *x, const uint16_t *plane, float *y, float scale,
+                     void *stream) {
+    if (!x || !plane || !y) return BLR_ERR_NULL;
+    if (M < 1 || n < 128 || k < 128 || n % 128 || k % 128) return BLR_ERR_SHAPE;
+    const int64_t widest = n > k ? n : k;
+    if (M * widest * 4 > (int64_t)0xFFFFFFFF || n * k * 2 > (int64_t)0xFFFFFFFF) return BLR_ERR_SHAPE;
+    if ((n / 128) * ceil_div(M, 64) > ((int64_t)1 << 31) - 1) return BLR_ERR_SHAPE;
+    if (!pow2_scale_ok(scale)) return BLR_ERR_SCALE;
+    if (!aligned16(x) || !aligned16(plane) || !aligned16(y)) return BLR_ERR_ALIGN;
+    int st = current_device_ok();
+    if (st != BLR_OK) return st;
+    GemmArgs a = {};
+    a.A = x;
+    a.lda = k;
+    a.ascale = scale;
+    a.Bplane = plane;
+    a.M = M;
+    a.N = (int)n;
+    a.K = (int)k;
+    a.oscale = 1.0f / scale;  // exact: scale is a power of two
+    a.out = y;
+    BLR_TRY(launch_gemm(GEMM_PLANE, a, (hipStream_t)stream));
+    return BLR_OK;
+}
+
 int blr_sumsq(const float *a, int64_t n, float *partials, int nparts, void *stream) {
     if (!a || !partials) return BLR_ERR_NULL;
     if (n < 1 || nparts < 1 || nparts > 1024) return BLR_ERR_SHAPE;

@@ -32,6 +32,7 @@ enum KernelId {
     K_GEMM_B1_DH, // B1 with dh fused (c recomputed per column block)
     K_GEMM_SIGNS, // sign gradients G_U, G_V (contractions over tokens)
     K_SUMSQ,      // sum-of-squares partials (finite check)
+    K_GEMM_PLANE, // dense frozen f16 linear
     K_COUNT
 };
 const char *kernel_name(int id);
@@ -45,6 +46,7 @@ struct GemmArgs {
     const float *colscale; // [K]
     float ascale;          // power of two
     const uint32_t *Bbits; // sign bitmap of the plane [N][K]: row n, word k/32, bit k%32 (set = +1)
+    const uint16_t *Bplane; // GEMM_PLANE: the f16 plane [N][K] itself (no column scale)
     int64_t M;
     int N, K;
     float oscale;          // power of two (1/ascale)
@@ -64,7 +66,7 @@ struct GemmArgs {
 
 // F2 writes the c tape and y (F2) or y only (F2_NOTAPE); DH repeats F2's
 // contraction with the same tiles (so c is bit-identical) and sums dy.c.
-enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_F2_NOTAPE, GEMM_B1, GEMM_B2, GEMM_DH, GEMM_B1_DH };
+enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_F2_NOTAPE, GEMM_B1, GEMM_B2, GEMM_DH, GEMM_B1_DH, GEMM_PLANE };
 // Rank columns per workgroup of GEMM_B1_DH (512, 256 or 128; the dh
 // partials have ceil(M/32) * (r / b1dh_cols(r)) rows).
 int b1dh_cols(int64_t r);

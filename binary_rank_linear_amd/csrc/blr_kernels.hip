@@ -247,7 +247,7 @@ hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, 
 }
 
 template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false,
-          int KB = 2>
+          int KB = 2, bool PLANE = false>
 __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     constexpr int NT = WM * WN * 64;  // threads of the contraction role
     constexpr int BK = 16 * KB;     // k per step: KB MFMA k-blocks, KB/2 bitmap words per plane row
@@ -262,6 +262,10 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % RPP == 0 && PER >= 1, "tile shape");
     static_assert((KB == 2 || KB == 4) && U % P == 0, "the register ring must divide the unroll");
     static_assert(!FDH || KB == 2, "fused dh walks 32-column steps");
+    // PLANE (dense frozen linear): the B fragments are read from an f16
+    // plane [N][K] (one 16-byte load per lane and k-block, one step ahead)
+    // instead of decoded from a bitmap, and the activation has no column scale.
+    static_assert(!PLANE || (!FDH && !DOT), "plane path shape");
     // Fused dh (B1 only): 32-row tiles, one row of waves, 128 ranks per wave,
     // and as many more waves in a second role (DH waves): they stage the f32
     // dy tile and compute the dh partials, so each SIMD holds one wave of
@@ -322,15 +326,18 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // the loads take a 32-bit per-lane offset plus a uniform offset, so no
     // VALU address arithmetic is needed.
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)M * p.lda * 4);
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.colscale, (uint64_t)K * 4);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.Bbits, (uint64_t)N * K / 8);
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.colscale, PLANE ? 0 : (uint64_t)K * 4);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.Bbits, PLANE ? 0 : (uint64_t)N * K / 8);
+    const __amdgpu_buffer_rsrc_t rP = make_rsrc(p.Bplane, PLANE ? (uint64_t)N * K * 2 : 0);
     const uint32_t coff = (uint32_t)c4 * 16;
     const int wofs = arow * LDK + c4 * 4;                                   // LDS write, halves
     const int rofs = (wm * TM + (lane & 31)) * LDK + (lane >> 5) * 8;      // fragment read, halves
     // Bitmap words of this lane's plane rows (one per 32-column block)
     uint32_t boff[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) boff[j] = (uint32_t)((int64_t)(n0 + wn * TN + j * 32 + (lane & 31)) * (K / 32) * 4);
+    for (int j = 0; j < FN; ++j)
+        boff[j] = PLANE ? (uint32_t)(((int64_t)(n0 + wn * TN + j * 32 + (lane & 31)) * K + (lane >> 5) * 8) * 2)
+                        : (uint32_t)((int64_t)(n0 + wn * TN + j * 32 + (lane & 31)) * (K / 32) * 4);
     // v_perm selectors: byte (2s + lane group) of the word into every byte
     const uint32_t grp = (uint32_t)(lane >> 5);
     const uint32_t sel[2] = {grp * 0x01010101u, (2u + grp) * 0x01010101u};
@@ -387,13 +394,13 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         const int k_ = (kt) < nk ? (kt) : nk - 1;                                          \
         _Pragma("unroll") for (int v = 0; v < PER; ++v) ar[q][v] =                         \
             load_f32x4(rA, aoff[v], (uint32_t)k_ * (BK * 4));                              \
-        cr[q] = load_f32x4(rC, coff, (uint32_t)k_ * (BK * 4));                             \
+        if (!PLANE) cr[q] = load_f32x4(rC, coff, (uint32_t)k_ * (BK * 4));                 \
     } while (0)
 
 #define BLR_BLOAD(dst, grp4)                                                               \
     do {                                                                                   \
         const int g_ = (grp4) < nk / U ? (grp4) : nk / U - 1;                              \
-        _Pragma("unroll") for (int j = 0; j < FN; ++j) dst[j] =                            \
+        if (!PLANE) _Pragma("unroll") for (int j = 0; j < FN; ++j) dst[j] =                \
             load_u32x4(rB, boff[j], (uint32_t)g_ * 16);                                    \
     } while (0)
 
@@ -409,7 +416,8 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                     dt_[(4 * c4 + e) * LDR] = in_ ? ar[q][v][e] : 0.0f;                    \
             }                                                                              \
         } else {                                                                           \
-            const f32x4_t cs_ = cr[q] * p.ascale;                                          \
+            const f32x4_t cs_ = PLANE ? f32x4_t{p.ascale, p.ascale, p.ascale, p.ascale}    \
+                                      : cr[q] * p.ascale;                                  \
             _Float16 *dst_ = As + (buf) * (BM * LDK) + wofs;                               \
             _Pragma("unroll") for (int v = 0; v < PER; ++v) {                              \
                 uint2 h_;                                                                  \
@@ -428,10 +436,12 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 *reinterpret_cast<const half8_t *>(src_ + i * 32 * LDK + s * 16);          \
     } while (0)
 
-#define BLR_BFRAG(dst, words, u)                                                           \
+#define BLR_BFRAG(dst, words, u, kstep)                                                    \
     do {                                                                                   \
+        const int kp_ = (kstep) < nk ? (kstep) : nk - 1;                                   \
         _Pragma("unroll") for (int j = 0; j < FN; ++j)                                     \
-            _Pragma("unroll") for (int s = 0; s < KB; ++s) dst[j][s] =                     \
+            _Pragma("unroll") for (int s = 0; s < KB; ++s) dst[j][s] = PLANE ?             \
+                __builtin_bit_cast(half8_t, load_u32x4(rP, boff[j], (uint32_t)(kp_ * BK + s * 16) * 2)) : \
                 sign_frag(words[j][(u) * (KB / 2) + s / 2], sel[s % 2], sgnmask, one16);   \
     } while (0)
 
@@ -498,7 +508,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         hb[0] = load_u32x4(rH, hoff, 0);
     } else {
         BLR_AFRAG(fa, 0);
-        BLR_BFRAG(fb, bq, 0);
+        BLR_BFRAG(fb, bq, 0, 0);
     }
     int b0 = 0, b1 = 1, b2 = 2;  // LDS buffers of steps kt, kt+1 and kt+2
 
@@ -536,14 +546,14 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 const int kt = kt0 + u;
                 if (u % 2 == 0) {
                     BLR_AFRAG(fa2, b1);
-                    BLR_BFRAG(fb2, bq, u + 1);
+                    BLR_BFRAG(fb2, bq, u + 1, kt + 1);
                     BLR_MMA(fa, fb);
                 } else {
                     BLR_AFRAG(fa, b1);
                     if (u < U - 1) {
-                        BLR_BFRAG(fb, bq, u + 1);
+                        BLR_BFRAG(fb, bq, u + 1, kt + 1);
                     } else {
-                        BLR_BFRAG(fb, bn, 0);
+                        BLR_BFRAG(fb, bn, 0, kt + 1);
                     }
                     BLR_MMA(fa2, fb2);
                 }
@@ -579,7 +589,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // rl + i*32 + 8*(v/4) + v%4 and column cb + j*32; the lane part of the
     // byte offset is a VGPR, the rest a uniform offset. Rows past M are
     // neither loaded, stored nor summed (only a tile that ends past M checks).
-    const float osc = -p.oscale;  // the fragments hold -S
+    const float osc = PLANE ? p.oscale : -p.oscale;  // decoded fragments hold -S
     const int64_t rl = m0 + wm * TM + 4 * (lane >> 5);
     const int cb = n0 + wn * TN + (lane & 31);
     const uint32_t loff = (uint32_t)((rl * N + cb) * 4);
@@ -648,12 +658,13 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 }
 
 template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false,
-          int KB = 2>
+          int KB = 2, bool PLANE = false>
 static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
     if (a.N % BN != 0 || a.K % 128 != 0 || a.K < 128) return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)(a.N / BN) * ((a.M + BM - 1) / BM);
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM, FDH, KB>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM, FDH, KB, PLANE>),
+                       dim3((unsigned)tiles),
                        dim3((FDH ? 2 : 1) * WM * WN * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     prof_end(s);
@@ -688,6 +699,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
         case GEMM_B2:
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s);
+        case GEMM_PLANE: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4, true>(K_GEMM_PLANE, a, s);
         case GEMM_B1_DH:
             switch (a.N) {  // one workgroup covers every rank: r / 128 waves of each role (1, 2 or 4)
                 case 128: return launch_gemm_t<32, 128, 1, 1, 1, 2, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
@@ -975,6 +987,7 @@ const char *kernel_name(int id) {
         case K_GEMM_B1_DH: return "gemm_b1_dh_fused";
         case K_GEMM_SIGNS: return "gemm_sign_grads";
         case K_SUMSQ: return "sumsq";
+        case K_GEMM_PLANE: return "gemm_plane_linear";
     }
     return "?";
 }

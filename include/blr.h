@@ -141,6 +141,18 @@ int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const 
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Dense frozen linear (page: `plane_linear`): y [M][n] = (f16(x * scale)
+ * . plane^T) / scale, x [M][k] f32, plane [n][k] f16 (IEEE binary16 bit
+ * patterns), through the same staging and MFMA contraction as the layer
+ * (f32 accumulation; y overwritten). scale is a positive finite power of two
+ * (the page stages gradients under a gradient scale when it runs this for
+ * the input gradient with the transposed plane). n and k multiples of 128,
+ * M >= 1; x, plane and y 16-byte aligned.
+ */
+int blr_plane_linear(int64_t M, int64_t n, int64_t k, const float *x, const uint16_t *plane, float *y, float scale,
+                     void *stream);
+
+/*
  * Sum of squares (page: `sumsq` shader and wrapper, the host's check of a
  * buffer for non-finite values): writes nparts f32 partial sums of a[i]^2,
  * i < n, to the device array partials[nparts]; the caller adds them (the

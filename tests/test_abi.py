@@ -217,3 +217,15 @@ def test_next_gscale_doubles_on_success_and_halves_on_overflow():
         g = blr.next_gscale(g, finite)
         m, e = np.frexp(g)
         assert m == 0.5  # stays a power of two
+
+
+def test_plane_linear_rejects_bad_arguments(ptrs):
+    lib = blr.load()
+    f = ptrs["_fake"]
+    good = (128, 256, 128, f(), f(), f(), ctypes.c_float(1.0), None)
+    assert lib.blr_plane_linear(128, 256, 128, None, f(), f(), ctypes.c_float(1.0), None) == E_NULL
+    assert lib.blr_plane_linear(128, 200, 128, f(), f(), f(), ctypes.c_float(1.0), None) == E_SHAPE
+    assert lib.blr_plane_linear(0, 256, 128, f(), f(), f(), ctypes.c_float(1.0), None) == E_SHAPE
+    assert lib.blr_plane_linear(128, 256, 128, f(), f(), f(), ctypes.c_float(3.0), None) == E_SCALE
+    assert lib.blr_plane_linear(128, 256, 128, f(offset=4), f(), f(), ctypes.c_float(1.0), None) == E_ALIGN
+    assert len(good) == 8
