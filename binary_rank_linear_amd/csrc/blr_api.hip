@@ -74,10 +74,12 @@ Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
     off += up((size_t)(r * ((d_in > d_out ? d_in : d_out) / 32)) * 4);
     L.db = off;
     off += up((size_t)(M * r) * 4);
-    // dh and dl partials: one row per 32 tokens covers every producer (the
-    // c-tape column sum, the recomputed-c contraction, B1 with dh fused)
+    // dh partials: 2 * ceil(M/64) rows (>= ceil(M/32)) cover every producer
+    // (the c-tape column sum, the recomputed-c contraction, B1 with dh fused
+    // on 32-token tiles or on 64-token tiles of two rank halves); dl
+    // partials: one row per 32 tokens
     L.part_h = off;
-    off += up((size_t)(ceil_div(M, PART_ROWS_MIN) * d_out) * 4);
+    off += up((size_t)(2 * ceil_div(M, GEMM_BM_MIN) * d_out) * 4);
     L.part_l = off;
     off += up((size_t)(ceil_div(M, PART_ROWS_MIN) * r) * 4);
     L.part_g = off;
@@ -256,8 +258,8 @@ static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, cons
     float *part_l = (float *)(ws + L.part_l);
     float *part_g = (float *)(ws + L.part_g);
     const float inv = 1.0f / gscale;  // exact: gscale is a power of two
-    const bool fused = tape_c == nullptr && b1dh_cols(r) == r;  // B1 with dh fused
-    const int64_t mt_b1 = ceil_div(M, gemm_tile_rows(fused ? GEMM_B1_DH : GEMM_B1));
+    const bool fused = tape_c == nullptr && b1dh_cols(r) > 0;  // B1 with dh fused
+    const int64_t mt_b1 = ceil_div(M, fused ? b1dh_tile_rows(r) : gemm_tile_rows(GEMM_B1));
     const int64_t mt_b2 = ceil_div(M, gemm_tile_rows(GEMM_B2));
 
     BLR_TRY(launch_transpose_bits(bits_u, d_out, r, bits_ut, s));
@@ -266,7 +268,8 @@ static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, cons
     // recomputed by F2's contraction (same tiles, so the same c)
     int64_t nparts_h = mt_b1;
     if (fused) {
-        // computed inside B1 below
+        // computed inside B1 below, one partial row per (row tile, rank tile)
+        nparts_h = mt_b1 * (r / b1dh_cols(r));
     } else if (tape_c) {
         BLR_TRY(launch_colsum(dy, tape_c, M, (int)d_out, part_h, s));
         nparts_h = ceil_div(M, COLSUM_ROWS);

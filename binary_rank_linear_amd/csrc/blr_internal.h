@@ -61,15 +61,18 @@ struct GemmArgs {
     const uint32_t *dh_bits; // bitmap of S_U [K][N/32] (K = d_out, N = r)
     const float *dh_a;       // the a tape [M][N]
     const float *dh_l;       // l [N]
-    float *dh_partial;       // [ceil(M/32) * (N/BN)][K]
+    float *dh_partial;       // [ceil(M/BM) * (N/BN)][K]
 };
 
 // F2 writes the c tape and y (F2) or y only (F2_NOTAPE); DH repeats F2's
 // contraction with the same tiles (so c is bit-identical) and sums dy.c.
 enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_F2_NOTAPE, GEMM_B1, GEMM_B2, GEMM_DH, GEMM_B1_DH, GEMM_PLANE };
-// Rank columns per workgroup of GEMM_B1_DH (512, 256 or 128; the dh
-// partials have ceil(M/32) * (r / b1dh_cols(r)) rows).
+// GEMM_B1_DH tiles: rank columns and token rows per workgroup (0 where the
+// fused launch does not serve r). The dh partials have
+// ceil(M / b1dh_tile_rows(r)) * (r / b1dh_cols(r)) rows, at most
+// 2 * ceil(M / 64); the dl partials ceil(M / b1dh_tile_rows(r)).
 int b1dh_cols(int64_t r);
+int b1dh_tile_rows(int64_t r);
 
 // Sign-plane expansion jobs (one bitmap each; pl and/or plt may be null).
 struct ExpandJob {

@@ -17,6 +17,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 // f16 bit patterns of +1 and -1.
@@ -172,6 +173,9 @@ __device__ __forceinline__ f32x4_t load_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ u32x4_t load_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+__device__ __forceinline__ u32x2_t load_u32x2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
 __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
@@ -266,16 +270,20 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // plane [N][K] (one 16-byte load per lane and k-block, one step ahead)
     // instead of decoded from a bitmap, and the activation has no column scale.
     static_assert(!PLANE || (!FDH && !DOT), "plane path shape");
-    // Fused dh (B1 only): 32-row tiles, one row of waves, 128 ranks per wave,
-    // and as many more waves in a second role (DH waves): they stage the f32
-    // dy tile and compute the dh partials, so each SIMD holds one wave of
-    // each role and one's VALU work overlaps the other's MFMAs.
-    static_assert(!FDH || (BM == 32 && WM == 1 && TN == 128 && DOT && OUT), "fused dh shape");
-    constexpr int LDR = 36;         // floats per row of the transposed f32 dy tile (pad: conflict-free)
+    // Fused dh (B1 only): 64-token tiles, one row of waves with 64 ranks
+    // each, and as many more waves in a second role (DH waves): they
+    // stage the f32 dy tile and compute the dh partials, so each SIMD holds
+    // one wave of each role and one's VALU work overlaps the other's MFMAs.
+    static_assert(!FDH || (WM == 1 && BM == 64 && TN == 64 && DOT && OUT), "fused dh shape");
+    constexpr int FMD = BM / 32;    // fused dh: row blocks of the recomputed c
+    constexpr int KD = TN / 16;     // fused dh: MFMA k-blocks over the wave's ranks (FMD * KD = 8)
+    constexpr int CP = 2 / FMD;     // fused dh: accumulators per row block (two MFMA chains in flight)
+    constexpr int LDR = BM + 4;     // floats per column of the transposed f32 dy tile (pad)
 
     __shared__ __attribute__((aligned(16))) _Float16 As[NS * BM * LDK];
     __shared__ float red[DOT ? WM * BN : 1];
-    __shared__ __attribute__((aligned(16))) float dyT[FDH ? NS * 32 * LDR : 1];  // [buf][column][row]
+    constexpr int NSD = 4;          // fused dh: depth of the dy ring (a step's dot runs one step late)
+    __shared__ __attribute__((aligned(16))) float dyT[FDH ? NSD * 32 * LDR : 1];  // [buf][column][row]
     __shared__ float redh[FDH ? 2 * WN * 32 : 1];                                // [step & 1][wave][column]
 
     const int tid = threadIdx.x;
@@ -346,31 +354,35 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     asm volatile("v_mov_b32 %0, 0x80008000" : "=v"(sgnmask));
     asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one16));
 
-    // Fused dh: the wave's A fragments f16(a * l) for its 128 ranks stay in
-    // registers (rows past M are zero, so they add nothing to dh), and each
-    // step reads the bitmap words of S_U rows i0 + (lane % 32), ranks of the
-    // wave: 4 words, one 16-byte load.
-    half8_t al[FDH ? 8 : 1];
+    // Fused dh: the wave's A fragments f16(a * l) (row block i, k-block t
+    // of its ranks at al[i * KD + t]) stay in registers (rows past M are
+    // zero, so they add nothing to dh), and each step reads the bitmap words
+    // of S_U rows i0 + (lane % 32), ranks of the wave: two words, one
+    // 8-byte load.
+    half8_t al[FDH ? FMD * KD : 1];
     uint32_t hoff = 0;
     const __amdgpu_buffer_rsrc_t rH = make_rsrc(p.dh_bits, FDH ? (uint64_t)K * N / 8 : 0);
     if (dhw) {
-        const int64_t gm = m0 + (lane & 31);
-        const bool inr = gm < M;
-        const float *ar_ = p.dh_a + (inr ? gm : 0) * N;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int k = n0 + wn * TN + 16 * t + 8 * (lane >> 5);
-            const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(ar_ + k);
-            const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(ar_ + k + 4);
-            const f32x4_t l0 = *reinterpret_cast<const f32x4_t *>(p.dh_l + k);
-            const f32x4_t l1 = *reinterpret_cast<const f32x4_t *>(p.dh_l + k + 4);
-            half8_t h;
+        for (int i = 0; i < FMD; ++i) {
+            const int64_t gm = m0 + 32 * i + (lane & 31);
+            const bool inr = gm < M;
+            const float *ar_ = p.dh_a + (inr ? gm : 0) * N;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                h[e] = inr ? (_Float16)(x0[e] * l0[e]) : (_Float16)0.0f;
-                h[4 + e] = inr ? (_Float16)(x1[e] * l1[e]) : (_Float16)0.0f;
+            for (int t = 0; t < KD; ++t) {
+                const int k = n0 + wn * TN + 16 * t + 8 * (lane >> 5);
+                const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(ar_ + k);
+                const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(ar_ + k + 4);
+                const f32x4_t l0 = *reinterpret_cast<const f32x4_t *>(p.dh_l + k);
+                const f32x4_t l1 = *reinterpret_cast<const f32x4_t *>(p.dh_l + k + 4);
+                half8_t h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = inr ? (_Float16)(x0[e] * l0[e]) : (_Float16)0.0f;
+                    h[4 + e] = inr ? (_Float16)(x1[e] * l1[e]) : (_Float16)0.0f;
+                }
+                al[i * KD + t] = h;
             }
-            al[t] = h;
         }
         hoff = (uint32_t)(((lane & 31) * (N / 32) + (n0 + wn * TN) / 32) * 4);
     }
@@ -407,13 +419,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 #define BLR_SSTORE(q, buf)                                                                 \
     do {                                                                                   \
         if (dhw) {                                                                         \
-            /* DH role: the f32 dy tile, transposed, rows past M zero */                   \
+            /* DH role: the f32 dy tile, transposed (rows past M hold row                  \
+               M-1, a finite copy: the recomputed c is zero there) */                      \
             _Pragma("unroll") for (int v = 0; v < PER; ++v) {                              \
-                const int r_ = arow + v * RPP;                                             \
-                const bool in_ = m0 + r_ < M;                                              \
-                float *dt_ = dyT + (buf) * (32 * LDR) + r_;                                \
-                _Pragma("unroll") for (int e = 0; e < 4; ++e)                              \
-                    dt_[(4 * c4 + e) * LDR] = in_ ? ar[q][v][e] : 0.0f;                    \
+                float *dt_ = dyT + (buf) * (32 * LDR) + arow + v * RPP;                    \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e) dt_[(4 * c4 + e) * LDR] = ar[q][v][e]; \
             }                                                                              \
         } else {                                                                           \
             const f32x4_t cs_ = PLANE ? f32x4_t{p.ascale, p.ascale, p.ascale, p.ascale}    \
@@ -454,39 +464,62 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     } while (0)
 
     // Fused dh, step kt (columns i0 = 32 kt of d_out): the wave's partial
-    // c over its ranks (8 MFMAs into two accumulators), times the f32 dy of
-    // the step, summed over the tile's rows; the two lane groups add, and
-    // the waves' sums go to redh for the first DH wave to add in wave order
-    // after the step's barrier (dh is linear in c, so per-wave partial c
-    // suffice).
-#define BLR_DH(HB, BUF, KT)                                                                \
+    // c over its ranks (8 MFMAs), times the f32 dy of the step, summed over
+    // the tile's rows; the two lane groups add, and the waves' sums go to
+    // redh for the first DH wave to add in wave order after the step's
+    // barrier (dh is linear in c, so per-wave partial c suffice). The role
+    // is software-pipelined: iteration kt issues the MFMAs of step kt,
+    // decodes the signs of step kt+1 and forms the dot of step kt-1, so the
+    // VALU work runs beside the MFMAs and no MFMA result is waited for.
+#define BLR_DH_DECODE(BF, HB)                                                              \
     do {                                                                                   \
-        f32x16_t c0_, c1_;                                                                 \
-        _Pragma("unroll") for (int v = 0; v < 16; ++v) c0_[v] = c1_[v] = 0.0f;             \
-        _Pragma("unroll") for (int t = 0; t < 8; t += 2) {                                 \
-            c0_ = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[t], sign_frag(HB[t / 2], sel[0], sgnmask, one16), c0_, 0, 0, 0); \
-            c1_ = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[t + 1], sign_frag(HB[t / 2], sel[1], sgnmask, one16), c1_, 0, 0, 0); \
-        }                                                                                  \
-        const float *dt_ = dyT + (BUF) * (32 * LDR) + (lane & 31) * LDR + 4 * (lane >> 5); \
-        float ds_ = 0.0f;                                                                  \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                    \
-            const f32x4_t d4_ = *reinterpret_cast<const f32x4_t *>(dt_ + 8 * q);           \
-            _Pragma("unroll") for (int e = 0; e < 4; ++e) ds_ += (c0_[4 * q + e] + c1_[4 * q + e]) * d4_[e]; \
-        }                                                                                  \
+        _Pragma("unroll") for (int t = 0; t < KD; ++t)                                     \
+            BF[t] = sign_frag(HB[t / 2], sel[t % 2], sgnmask, one16);                      \
+    } while (0)
+#define BLR_DH_MMA(CC, BF)                                                                 \
+    do {                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < FMD; ++i)                                    \
+            _Pragma("unroll") for (int q = 0; q < CP; ++q)                                 \
+                _Pragma("unroll") for (int v = 0; v < 16; ++v) CC[i][q][v] = 0.0f;         \
+        _Pragma("unroll") for (int t = 0; t < KD; ++t)                                     \
+            _Pragma("unroll") for (int i = 0; i < FMD; ++i) CC[i][t % CP] =                \
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i * KD + t], BF[t], CC[i][t % CP], 0, 0, 0); \
+    } while (0)
+#define BLR_DH_DYLOAD(D4, BUF)                                                             \
+    do {                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < FMD; ++i)                                    \
+            _Pragma("unroll") for (int q = 0; q < 4; ++q) D4[i][q] =                       \
+                *reinterpret_cast<const f32x4_t *>(dyT + (BUF) * (32 * LDR) + (lane & 31) * LDR + \
+                                                   32 * i + 4 * (lane >> 5) + 8 * q);      \
+    } while (0)
+#define BLR_DH_DOT(CC, D4, KT)                                                             \
+    do {                                                                                   \
+        float dq_[4] = {0.0f, 0.0f, 0.0f, 0.0f}; /* four independent chains */            \
+        _Pragma("unroll") for (int i = 0; i < FMD; ++i)                                    \
+            _Pragma("unroll") for (int q = 0; q < 4; ++q)                                  \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e) {                            \
+                    float c_ = CC[i][0][4 * q + e];                                        \
+                    _Pragma("unroll") for (int q2 = 1; q2 < CP; ++q2) c_ += CC[i][q2][4 * q + e]; \
+                    dq_[q] += c_ * D4[i][q][e];                                            \
+                }                                                                          \
+        float ds_ = (dq_[0] + dq_[1]) + (dq_[2] + dq_[3]);                                 \
         ds_ += __shfl_xor(ds_, 32);                                                        \
-        if (lane < 32) redh[((KT) & 1) * (WN * 32) + wn * 32 + lane] = ds_;                \
+        redh[((KT) & 1) * (WN * 32) + wn * 32 + (lane & 31)] = ds_;                        \
     } while (0)
     // the first DH wave adds the waves' dh sums of step KT (after that
     // step's barrier);
     // the fragments hold -S, hence the sign
+    // Straight-line (no branch splits the DH iteration): every DH lane adds
+    // the sums of its column, and only lanes 0-31 of the first DH wave, for
+    // a step >= 0, store; the others' byte offset lies past the partials'
+    // buffer range, and the buffer unit drops an out-of-range store.
 #define BLR_DH_STORE(KT)                                                                   \
     do {                                                                                   \
-        if (dhw && rwave == 0 && lane < 32) {                                              \
-            const float *rr_ = redh + ((KT) & 1) * (WN * 32);                              \
-            float s_ = 0.0f;                                                               \
-            _Pragma("unroll") for (int w = 0; w < WN; ++w) s_ += rr_[w * 32 + lane];       \
-            p.dh_partial[((int64_t)mt * ntn + nt) * K + (int64_t)(KT) * 32 + lane] = -s_;  \
-        }                                                                                  \
+        const float *rr_ = redh + ((KT) & 1) * (WN * 32) + (lane & 31);                    \
+        float s_ = 0.0f;                                                                   \
+        _Pragma("unroll") for (int w = 0; w < WN; ++w) s_ += rr_[w * 32];                  \
+        const bool st_ = rwave == 0 && lane < 32 && (KT) >= 0;                             \
+        store_f32(rHP, st_ ? hpoff + (uint32_t)(KT) * 128u : 0xFFFFFF00u, 0u, -s_);        \
     } while (0)
 
     // Prologue: stages 0 and 1 into LDS buffers 0 and 1, the register ring
@@ -503,9 +536,14 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     BLR_SSTORE(1 % P, 1);
     BLR_GLOAD(1 % P, P + 1);
     __syncthreads();
-    u32x4_t hb[2];               // dh bitmap words of steps kt and kt+1
+    u32x2_t hb[2];               // dh bitmap words (the wave's 64 ranks) of two steps
+#define BLR_HLOAD(dst, soff_) dst = load_u32x2(rH, hoff, (soff_))
+    // dh partial row (mt, nt): byte offset of column `lane` of step 0
+    const uint64_t hpbytes = FDH ? (uint64_t)((M + BM - 1) / BM) * ntn * K * 4 : 0;
+    const __amdgpu_buffer_rsrc_t rHP = make_rsrc(p.dh_partial, hpbytes);
+    const uint32_t hpoff = (uint32_t)((((int64_t)mt * ntn + nt) * K + (lane & 31)) * 4);
     if (dhw) {
-        hb[0] = load_u32x4(rH, hoff, 0);
+        BLR_HLOAD(hb[0], 0u);
     } else {
         BLR_AFRAG(fa, 0);
         BLR_BFRAG(fb, bq, 0, 0);
@@ -519,24 +557,53 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // last one and are never multiplied), so the compiler counts outstanding
     // loads exactly and waits only for the stage it converts.
     if (dhw) {
-        // DH role: per step the partial c of the wave's ranks and its dh sums
+        // DH role, per step the partial c of the wave's ranks and its dh
+        // sums. Iteration kt: MFMAs of step kt, signs of step kt+1 (words
+        // loaded an iteration ago), words of step kt+2, the dot of step kt-1
+        // (its dy in ring slot (kt-1) % 4, rewritten only after this
+        // iteration's barrier), the dh store of step kt-2, and stage kt+2.
+        // The iteration is one basic block: the dot of step -1 (iteration 0)
+        // multiplies a zero c by whatever slot 3 holds, and its sums and the
+        // stores of steps -2 and -1 are never kept.
+        half8_t hf[2][KD];       // decoded signs of steps kt and kt+1
+        f32x16_t cc[2][FMD][CP]; // partial c of steps kt and kt-1
+        f32x4_t d4[FMD][4];      // dy of step kt-1 in the accumulator layout
+#pragma unroll
+        for (int i = 0; i < FMD; ++i)
+#pragma unroll
+            for (int q = 0; q < CP; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) cc[1][i][q][v] = 0.0f;
+        BLR_HLOAD(hb[1], (uint32_t)(nk > 1 ? 1 : 0) * N * 4);
+        BLR_DH_DECODE(hf[0], hb[0]);
         for (int kt0 = 0; kt0 < nk; kt0 += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int kt = kt0 + u;
-                const int kn_ = kt + 1 < nk ? kt + 1 : nk - 1;
-                hb[(u + 1) & 1] = load_u32x4(rH, hoff, (uint32_t)kn_ * N * 4);
-                if (kt > 0) BLR_DH_STORE(kt - 1);
-                BLR_DH(hb[u & 1], b0, kt);
-                BLR_SSTORE((u + 2) % P, b2);
+                BLR_DH_DYLOAD(d4, (kt + NSD - 1) & (NSD - 1));
+                BLR_DH_MMA(cc[u & 1], hf[u & 1]);
+                BLR_DH_DECODE(hf[(u + 1) & 1], hb[(u + 1) & 1]);
+                const int kn_ = kt + 2 < nk ? kt + 2 : nk - 1;
+                BLR_HLOAD(hb[u & 1], (uint32_t)kn_ * N * 4);
+                BLR_DH_DOT(cc[(u + 1) & 1], d4, kt - 1);
+                BLR_DH_STORE(kt - 2);
+                BLR_SSTORE((u + 2) % P, (kt + 2) & (NSD - 1));
                 BLR_GLOAD((u + 2) % P, kt + 2 + P);
+                // the dy reads first, then each MFMA followed by VALU work
+                // (decode, dot, sums), which issues while the MFMA runs
+                __builtin_amdgcn_sched_group_barrier(0x100, 8 * FMD / 2, 0);
+#pragma unroll
+                for (int m_ = 0; m_ < 8; ++m_) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                }
                 __syncthreads();
                 __builtin_amdgcn_sched_barrier(0);
-                b0 = b1;
-                b1 = b2;
-                b2 = b2 == NS - 1 ? 0 : b2 + 1;
             }
         }
+        BLR_DH_DYLOAD(d4, (nk - 1) & (NSD - 1));
+        BLR_DH_DOT(cc[1], d4, nk - 1);  // nk is a multiple of 4: step nk-1 is odd
+        BLR_DH_STORE(nk - 2);
         __syncthreads();
         BLR_DH_STORE(nk - 1);
     } else {
@@ -575,8 +642,12 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         }
         if (FDH) __syncthreads();  // matches the DH role's final barrier
     }
-#undef BLR_DH
+#undef BLR_DH_DYLOAD
+#undef BLR_DH_DECODE
+#undef BLR_DH_MMA
+#undef BLR_DH_DOT
 #undef BLR_DH_STORE
+#undef BLR_HLOAD
 #undef BLR_GLOAD
 #undef BLR_BLOAD
 #undef BLR_SSTORE
@@ -680,7 +751,8 @@ static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
 // groups of 8 M tiles per N tile. Every kind uses 64-row tiles, so the
 // column partials have ceil(M/64) rows.
 int gemm_tile_rows(GemmKind kind) { return kind == GEMM_B1_DH ? 32 : 64; }
-int b1dh_cols(int64_t r) { return (r == 128 || r == 256 || r == 512) ? (int)r : 0; }
+int b1dh_cols(int64_t r) { return (r == 128 || r == 256) ? (int)r : r == 512 ? 256 : 0; }
+int b1dh_tile_rows(int64_t r) { return b1dh_cols(r) ? 64 : 0; }
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     const bool wide = a.N % 256 == 0;
@@ -701,10 +773,10 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s);
         case GEMM_PLANE: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4, true>(K_GEMM_PLANE, a, s);
         case GEMM_B1_DH:
-            switch (a.N) {  // one workgroup covers every rank: r / 128 waves of each role (1, 2 or 4)
-                case 128: return launch_gemm_t<32, 128, 1, 1, 1, 2, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
-                case 256: return launch_gemm_t<32, 256, 1, 2, 1, 2, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
-                case 512: return launch_gemm_t<32, 512, 1, 4, 1, 2, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
+            switch (a.N) {  // 64 tokens x up to 256 ranks, 64 ranks per wave
+                case 128: return launch_gemm_t<64, 128, 1, 2, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
+                case 256:
+                case 512: return launch_gemm_t<64, 256, 1, 4, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
             }
             return hipErrorInvalidValue;
     }
