@@ -284,7 +284,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     __shared__ float red[DOT ? WM * BN : 1];
     constexpr int NSD = 4;          // fused dh: depth of the dy ring (a step's dot runs one step late)
     __shared__ __attribute__((aligned(16))) float dyT[FDH ? NSD * 32 * LDR : 1];  // [buf][column][row]
-    __shared__ float redh[FDH ? 2 * WN * 32 : 1];                                // [step & 1][wave][column]
+    __shared__ float redh[FDH ? 2 * WN * 64 : 1];                                // [step & 1][wave][lane]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -406,7 +406,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         const int k_ = (kt) < nk ? (kt) : nk - 1;                                          \
         _Pragma("unroll") for (int v = 0; v < PER; ++v) ar[q][v] =                         \
             load_f32x4(rA, aoff[v], (uint32_t)k_ * (BK * 4));                              \
-        if (!PLANE) cr[q] = load_f32x4(rC, coff, (uint32_t)k_ * (BK * 4));                 \
+        if (!PLANE && !dhw) cr[q] = load_f32x4(rC, coff, (uint32_t)k_ * (BK * 4));         \
     } while (0)
 
 #define BLR_BLOAD(dst, grp4)                                                               \
@@ -420,9 +420,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     do {                                                                                   \
         if (dhw) {                                                                         \
             /* DH role: the f32 dy tile, transposed (rows past M hold row                  \
-               M-1, a finite copy: the recomputed c is zero there) */                      \
+               M-1, a finite copy: the recomputed c is zero there); row bit 3 is           \
+               flipped in columns 16-31, which spreads a write's 64 lanes                  \
+               over distinct banks */                                                      \
             _Pragma("unroll") for (int v = 0; v < PER; ++v) {                              \
-                float *dt_ = dyT + (buf) * (32 * LDR) + arow + v * RPP;                    \
+                float *dt_ = dyT + (buf) * (32 * LDR) + ((arow + v * RPP) ^ (8 * (c4 >> 2))); \
                 _Pragma("unroll") for (int e = 0; e < 4; ++e) dt_[(4 * c4 + e) * LDR] = ar[q][v][e]; \
             }                                                                              \
         } else {                                                                           \
@@ -465,9 +467,9 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 
     // Fused dh, step kt (columns i0 = 32 kt of d_out): the wave's partial
     // c over its ranks (8 MFMAs), times the f32 dy of the step, summed over
-    // the tile's rows; the two lane groups add, and the waves' sums go to
-    // redh for the first DH wave to add in wave order after the step's
-    // barrier (dh is linear in c, so per-wave partial c suffice). The role
+    // the lane's rows; every lane's sum goes to redh, and after the step's
+    // barrier the first DH wave adds them in wave and lane-group order (dh
+    // is linear in c, so per-wave partial c suffice). The role
     // is software-pipelined: iteration kt issues the MFMAs of step kt,
     // decodes the signs of step kt+1 and forms the dot of step kt-1, so the
     // VALU work runs beside the MFMAs and no MFMA result is waited for.
@@ -490,7 +492,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         _Pragma("unroll") for (int i = 0; i < FMD; ++i)                                    \
             _Pragma("unroll") for (int q = 0; q < 4; ++q) D4[i][q] =                       \
                 *reinterpret_cast<const f32x4_t *>(dyT + (BUF) * (32 * LDR) + (lane & 31) * LDR + \
-                                                   32 * i + 4 * (lane >> 5) + 8 * q);      \
+                                                   32 * i + 4 * (lane >> 5) + 8 * (q ^ ((lane >> 4) & 1))); \
     } while (0)
 #define BLR_DH_DOT(CC, D4, KT)                                                             \
     do {                                                                                   \
@@ -502,22 +504,28 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                     _Pragma("unroll") for (int q2 = 1; q2 < CP; ++q2) c_ += CC[i][q2][4 * q + e]; \
                     dq_[q] += c_ * D4[i][q][e];                                            \
                 }                                                                          \
-        float ds_ = (dq_[0] + dq_[1]) + (dq_[2] + dq_[3]);                                 \
-        ds_ += __shfl_xor(ds_, 32);                                                        \
-        redh[((KT) & 1) * (WN * 32) + wn * 32 + (lane & 31)] = ds_;                        \
+        redh[((KT) & 1) * (WN * 64) + wn * 64 + lane] = (dq_[0] + dq_[1]) + (dq_[2] + dq_[3]); \
     } while (0)
     // the first DH wave adds the waves' dh sums of step KT (after that
     // step's barrier);
     // the fragments hold -S, hence the sign
     // Straight-line (no branch splits the DH iteration): every DH lane adds
-    // the sums of its column, and only lanes 0-31 of the first DH wave, for
-    // a step >= 0, store; the others' byte offset lies past the partials'
-    // buffer range, and the buffer unit drops an out-of-range store.
-#define BLR_DH_STORE(KT)                                                                   \
+    // the sums of its column (two lanes per wave hold rows of one column),
+    // and only lanes 0-31 of the first DH wave, for a step >= 0, store; the
+    // others' byte offset lies past the partials' buffer range, and the
+    // buffer unit drops an out-of-range store.
+#define BLR_DH_SUMLOAD(RS, KT)                                                             \
     do {                                                                                   \
-        const float *rr_ = redh + ((KT) & 1) * (WN * 32) + (lane & 31);                    \
+        const float *rr_ = redh + ((KT) & 1) * (WN * 64) + (lane & 31);                    \
+        _Pragma("unroll") for (int w = 0; w < WN; ++w) {                                   \
+            RS[2 * w] = rr_[w * 64];                                                       \
+            RS[2 * w + 1] = rr_[w * 64 + 32];                                              \
+        }                                                                                  \
+    } while (0)
+#define BLR_DH_STORE(RS, KT)                                                               \
+    do {                                                                                   \
         float s_ = 0.0f;                                                                   \
-        _Pragma("unroll") for (int w = 0; w < WN; ++w) s_ += rr_[w * 32];                  \
+        _Pragma("unroll") for (int w = 0; w < WN; ++w) s_ += RS[2 * w] + RS[2 * w + 1];    \
         const bool st_ = rwave == 0 && lane < 32 && (KT) >= 0;                             \
         store_f32(rHP, st_ ? hpoff + (uint32_t)(KT) * 128u : 0xFFFFFF00u, 0u, -s_);        \
     } while (0)
@@ -525,6 +533,15 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // Prologue: stages 0 and 1 into LDS buffers 0 and 1, the register ring
     // refilled behind them, the bitmap words of groups 0 and 1, and the
     // fragments of step 0.
+    u32x2_t hb[2];               // dh bitmap words (the wave's 64 ranks) of two steps
+#define BLR_HLOAD(dst, soff_) dst = load_u32x2(rH, hoff, (soff_))
+    // (the DH role's words of steps 0 and 1 go first: the loop then finds
+    // as many loads issued after them as in its steady state, and waits for
+    // no more than those)
+    if (dhw) {
+        BLR_HLOAD(hb[0], 0u);
+        BLR_HLOAD(hb[1], (uint32_t)(nk > 1 ? 1 : 0) * N * 4);
+    }
 #pragma unroll
     for (int q = 0; q < P; ++q) BLR_GLOAD(q, q);
     if (!dhw) {
@@ -536,15 +553,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     BLR_SSTORE(1 % P, 1);
     BLR_GLOAD(1 % P, P + 1);
     __syncthreads();
-    u32x2_t hb[2];               // dh bitmap words (the wave's 64 ranks) of two steps
-#define BLR_HLOAD(dst, soff_) dst = load_u32x2(rH, hoff, (soff_))
     // dh partial row (mt, nt): byte offset of column `lane` of step 0
     const uint64_t hpbytes = FDH ? (uint64_t)((M + BM - 1) / BM) * ntn * K * 4 : 0;
     const __amdgpu_buffer_rsrc_t rHP = make_rsrc(p.dh_partial, hpbytes);
     const uint32_t hpoff = (uint32_t)((((int64_t)mt * ntn + nt) * K + (lane & 31)) * 4);
-    if (dhw) {
-        BLR_HLOAD(hb[0], 0u);
-    } else {
+    if (!dhw) {
         BLR_AFRAG(fa, 0);
         BLR_BFRAG(fb, bq, 0, 0);
     }
@@ -574,24 +587,25 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
             for (int q = 0; q < CP; ++q)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) cc[1][i][q][v] = 0.0f;
-        BLR_HLOAD(hb[1], (uint32_t)(nk > 1 ? 1 : 0) * N * 4);
         BLR_DH_DECODE(hf[0], hb[0]);
         for (int kt0 = 0; kt0 < nk; kt0 += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int kt = kt0 + u;
+                float rs[2 * WN];  // the dh sums of step kt-2
                 BLR_DH_DYLOAD(d4, (kt + NSD - 1) & (NSD - 1));
+                BLR_DH_SUMLOAD(rs, kt - 2);
                 BLR_DH_MMA(cc[u & 1], hf[u & 1]);
                 BLR_DH_DECODE(hf[(u + 1) & 1], hb[(u + 1) & 1]);
                 const int kn_ = kt + 2 < nk ? kt + 2 : nk - 1;
                 BLR_HLOAD(hb[u & 1], (uint32_t)kn_ * N * 4);
+                BLR_DH_STORE(rs, kt - 2);
                 BLR_DH_DOT(cc[(u + 1) & 1], d4, kt - 1);
-                BLR_DH_STORE(kt - 2);
                 BLR_SSTORE((u + 2) % P, (kt + 2) & (NSD - 1));
                 BLR_GLOAD((u + 2) % P, kt + 2 + P);
                 // the dy reads first, then each MFMA followed by VALU work
                 // (decode, dot, sums), which issues while the MFMA runs
-                __builtin_amdgcn_sched_group_barrier(0x100, 8 * FMD / 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 * FMD + WN, 0);
 #pragma unroll
                 for (int m_ = 0; m_ < 8; ++m_) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -601,11 +615,14 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        float rs[2 * WN];
         BLR_DH_DYLOAD(d4, (nk - 1) & (NSD - 1));
+        BLR_DH_SUMLOAD(rs, nk - 2);
+        BLR_DH_STORE(rs, nk - 2);
         BLR_DH_DOT(cc[1], d4, nk - 1);  // nk is a multiple of 4: step nk-1 is odd
-        BLR_DH_STORE(nk - 2);
         __syncthreads();
-        BLR_DH_STORE(nk - 1);
+        BLR_DH_SUMLOAD(rs, nk - 1);
+        BLR_DH_STORE(rs, nk - 1);
     } else {
         for (int kt0 = 0; kt0 < nk; kt0 += U) {
 #pragma unroll
@@ -646,6 +663,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 #undef BLR_DH_DECODE
 #undef BLR_DH_MMA
 #undef BLR_DH_DOT
+#undef BLR_DH_SUMLOAD
 #undef BLR_DH_STORE
 #undef BLR_HLOAD
 #undef BLR_GLOAD
