@@ -760,6 +760,241 @@ static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
     return e;
 }
 
+// ---------------------------------------------------------------------------
+// Short-K contraction with the activation block held in LDS (the kinds with
+// K = r: F2, B2). A workgroup of 4 waves loads the bitmap words of all its
+// tiles into registers, stages its 64 x K activation rows once (scaled and
+// rounded to f16, as in gemm_kernel), then walks a run of TPW consecutive
+// 64 x 256 output tiles with no further barrier and no load before its
+// epilogue: per tile each wave (64 rows x 64 columns) reads A fragments
+// from LDS, decodes B fragments from its words, and stores its block from
+// the accumulators, so one tile's stores drain while the next tile's MFMAs
+// run (a load issued after the stores would have to wait for them: vector
+// loads and stores share one counter). The column partials need no
+// cross-wave sum: every wave holds all 64 rows of its columns.
+constexpr int AS_BM = 64, AS_BN = 256, AS_KMAX = 512;  // LDS: 64 x (K + 8) halves, 66.5 KB at K = 512
+
+template <int KG, int TPW, bool OUT, bool OUT2, bool DOT>
+__global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_n) {
+    constexpr int K = 128 * KG, LDK = K + 8;
+    __shared__ __attribute__((aligned(16))) _Float16 As[AS_BM * LDK];
+    constexpr int FM = 2, FN = 2, TN = 64;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = p.N;
+    const int64_t M = p.M;
+    const int L = blockIdx.x, G = gridDim.x;
+    const int T = (G % NUM_XCD == 0) ? (L % NUM_XCD) * (G / NUM_XCD) + L / NUM_XCD : L;
+    const int mt = T / groups_n, gn = T - mt * groups_n;
+    const int t0 = gn * TPW;  // the workgroup's tiles: t0 .. t0 + TPW - 1
+    const int64_t m0 = (int64_t)mt * AS_BM;
+
+    // bitmap words of this lane's two plane rows in each tile, KG 16-byte
+    // groups per row; tile 0's first (they arrive while the block is
+    // staged), each later tile's at the start of the one before
+    constexpr int KW = K / 32;  // bitmap words per plane row
+    u32x4_t wall[TPW][2][KG];
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.Bbits, (uint64_t)N * K / 8);
+#define AS_WLOAD(tt)                                                                       \
+    do {                                                                                   \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                    \
+            const uint32_t bo_ = (uint32_t)(((t0 + (tt)) * AS_BN + wn * 64 + j * 32 + (lane & 31)) * KW * 4); \
+            _Pragma("unroll") for (int g = 0; g < KG; ++g) wall[tt][j][g] = load_u32x4(rB, bo_, (uint32_t)g * 16); \
+        }                                                                                  \
+    } while (0)
+    AS_WLOAD(0);
+
+    // Stage the block: chunk i (float4) of the 64 x K block is row i / (K/4),
+    // columns 4 (i % (K/4)); rows past M read row M-1 (never stored or summed).
+    {
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)M * p.lda * 4);
+        const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.colscale, (uint64_t)K * 4);
+        constexpr int cpr = K / 4, nch = AS_BM * cpr;  // chunks per row, in the block
+        constexpr int UNR = 8;
+        for (int i0 = 0; i0 < nch; i0 += 256 * UNR) {
+            f32x4_t v[UNR], c[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int i = i0 + u * 256 + tid;
+                const int ic = i < nch ? i : nch - 1;
+                const int row = ic / cpr, c4 = ic - row * cpr;
+                int64_t gm = m0 + row;
+                gm = gm < M ? gm : M - 1;
+                v[u] = load_f32x4(rA, (uint32_t)((gm * p.lda + 4 * c4) * 4), 0u);
+                c[u] = load_f32x4(rC, (uint32_t)(16 * c4), 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int i = i0 + u * 256 + tid;
+                if (i < nch) {
+                    const int row = i / cpr, c4 = i - row * cpr;
+                    const f32x4_t cs = c[u] * p.ascale;
+                    uint2 h;
+                    h.x = f16x2_scaled(v[u].x, cs.x, v[u].y, cs.y);
+                    h.y = f16x2_scaled(v[u].z, cs.z, v[u].w, cs.w);
+                    *reinterpret_cast<uint2 *>(As + row * LDK + 4 * c4) = h;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const uint32_t grp = (uint32_t)(lane >> 5);
+    const uint32_t sel[2] = {grp * 0x01010101u, (2u + grp) * 0x01010101u};
+    uint32_t sgnmask, one16;
+    asm volatile("v_mov_b32 %0, 0x80008000" : "=v"(sgnmask));
+    asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one16));
+    const _Float16 *arow = As + (lane & 31) * LDK + (lane >> 5) * 8;  // fragment read base
+
+    const float osc = -p.oscale;  // decoded fragments hold -S
+    const uint64_t obytes = (uint64_t)M * N * 4;
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(p.out, OUT ? obytes : 0);
+    const __amdgpu_buffer_rsrc_t rO2 = make_rsrc(p.out2, OUT2 ? obytes : 0);
+    const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.dot_other, DOT ? obytes : 0);
+    const int64_t rl = m0 + 4 * (lane >> 5);
+    const bool full = m0 + AS_BM <= M;
+
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int t = t0 + tt;
+        if (tt + 1 < TPW) AS_WLOAD(tt + 1);
+        f32x16_t acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+        // k-blocks of 16 (word kb/2 of group kb/8): the A fragments and signs
+        // of block kb+1 are read and decoded while block kb's MFMAs run
+        constexpr int NKB = 8 * KG;
+        half8_t fa[2][FM], fb[2][FN];
+#define AS_FRAGS(buf, kb)                                                                  \
+        do {                                                                               \
+            _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[buf][i] =                    \
+                *reinterpret_cast<const half8_t *>(arow + i * 32 * LDK + 16 * (kb));       \
+            _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[buf][j] =                    \
+                sign_frag(wall[tt][j][(kb) / 8][((kb) / 2) % 4], sel[(kb) % 2], sgnmask, one16); \
+        } while (0)
+        AS_FRAGS(0, 0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            if (kb + 1 < NKB) AS_FRAGS((kb + 1) & 1, kb + 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[kb & 1][i], fb[kb & 1][j], acc[i][j], 0, 0, 0);
+            // this block: the next block's reads first, then MFMAs with the
+            // decode in between
+            if (kb + 1 < NKB) {
+                __builtin_amdgcn_sched_group_barrier(0x100, FM, 0);
+#pragma unroll
+                for (int m_ = 0; m_ < FM * FN; ++m_) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#undef AS_FRAGS
+        // epilogue: element (i, v, j) at row rl + 32 i + 8 (v/4) + v%4, column cb + 32 j;
+        // the row stride is re-read per tile (opaque to the compiler), so its
+        // 64 uniform offsets are formed here rather than held across tiles
+        int Nl = N;
+        asm volatile("" : "+s"(Nl));
+        const int cb = t * AS_BN + wn * TN + (lane & 31);
+        const uint32_t loff = (uint32_t)((rl * Nl + cb) * 4);
+        float c2[FN], dsum[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            c2[j] = OUT2 ? p.out2col[cb + j * 32] : 0.0f;
+            dsum[j] = 0.0f;
+        }
+#define AS_UOFF(i, v, j) ((uint32_t)((8 * ((v) >> 2) + ((v) & 3)) * Ni + (j) * 32) * 4u)
+#define AS_EPI(GUARD)                                                                      \
+        do {                                                                               \
+            _Pragma("unroll") for (int i = 0; i < FM; ++i) {                               \
+                /* one row block at a time: 16 uniform row offsets live */                  \
+                int Ni = Nl;                                                               \
+                asm volatile("" : "+s"(Ni));                                               \
+                const uint32_t lo_ = loff + (uint32_t)(i * 32 * Ni * 4);                   \
+                float oth[DOT ? FN : 1][DOT ? 16 : 1], old[OUT2 ? FN : 1][OUT2 ? 16 : 1];  \
+                _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+                    const bool in_ = !(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M; \
+                    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                       \
+                        if (DOT) oth[j][v] = in_ ? load_f32_nt(rD, lo_, AS_UOFF(i, v, j)) : 0.0f; \
+                        if (OUT2) old[j][v] = (p.out2acc && in_) ? load_f32(rO2, lo_, AS_UOFF(i, v, j)) : 0.0f; \
+                    }                                                                      \
+                }                                                                          \
+                _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+                    if (!(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M) {            \
+                        _Pragma("unroll") for (int j = 0; j < FN; ++j) {                   \
+                            const float val = acc[i][j][v] * osc;                          \
+                            if (OUT) store_f32(rO, lo_, AS_UOFF(i, v, j), val);           \
+                            if (OUT2) store_f32_nt(rO2, lo_, AS_UOFF(i, v, j), old[j][v] + val * c2[j]); \
+                            if (DOT) dsum[j] += val * oth[j][v];                           \
+                        }                                                                  \
+                    }                                                                      \
+                }                                                                          \
+            }                                                                              \
+        } while (0)
+        if (full) {
+            AS_EPI(false);
+        } else {
+            AS_EPI(true);
+        }
+#undef AS_EPI
+#undef AS_UOFF
+        if (DOT) {
+            // lanes l and l+32 hold other rows of the same column
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const float sum = dsum[j] + __shfl_xor(dsum[j], 32);
+                if (lane < 32) p.dot_partial[(int64_t)mt * N + cb + j * 32] = sum;
+            }
+        }
+    }
+#undef AS_WLOAD
+}
+
+template <int KG, int TPW, bool OUT, bool OUT2, bool DOT>
+static hipError_t launch_gemm_as_tt(int id, const GemmArgs &a, hipStream_t s) {
+    const int64_t mtiles = (a.M + AS_BM - 1) / AS_BM;
+    const int64_t gn = a.N / AS_BN / TPW;
+    prof_begin(id, s);
+    hipLaunchKernelGGL((gemm_as_kernel<KG, TPW, OUT, OUT2, DOT>), dim3((unsigned)(mtiles * gn)), dim3(256), 0, s, a,
+                       (int)gn);
+    hipError_t e = hipGetLastError();
+    prof_end(s);
+    return e;
+}
+
+template <int KG, bool OUT, bool OUT2, bool DOT>
+static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
+    if (a.N % AS_BN != 0 || a.K != 128 * KG) return hipErrorInvalidValue;
+    const int64_t mtiles = (a.M + AS_BM - 1) / AS_BM;
+    const int ntiles = a.N / AS_BN;
+    // the longest run of tiles (its words fit in registers: TPW * KG <= 16)
+    // that still gives about two workgroups per CU; the runs of one M tile
+    // land on one XCD
+    if (KG <= 4 && ntiles % 4 == 0 && mtiles * (ntiles / 4) >= 512)
+        return launch_gemm_as_tt<KG, 4, OUT, OUT2, DOT>(id, a, s);
+    if (ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 512) return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT>(id, a, s);
+    return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT>(id, a, s);
+}
+
+template <bool OUT, bool OUT2, bool DOT>
+static hipError_t launch_gemm_as(int id, const GemmArgs &a, hipStream_t s) {
+    switch (a.K) {
+        case 128: return launch_gemm_as_t<1, OUT, OUT2, DOT>(id, a, s);
+        case 256: return launch_gemm_as_t<2, OUT, OUT2, DOT>(id, a, s);
+        case 384: return launch_gemm_as_t<3, OUT, OUT2, DOT>(id, a, s);
+        case 512: return launch_gemm_as_t<4, OUT, OUT2, DOT>(id, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 // Tile shapes per kind (measured at M=8192, d=4096, r=512): 64-row tiles of
 // 1x4 waves, two workgroups per CU so that one's prologue and epilogue
 // overlap the other's main loop, and K steps of 64 (one barrier per 4 MFMA
@@ -774,12 +1009,15 @@ int b1dh_tile_rows(int64_t r) { return b1dh_cols(r) ? 64 : 0; }
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     const bool wide = a.N % 256 == 0;
+    const bool as = wide && a.K <= AS_KMAX;  // activation block held in LDS
     switch (kind) {
         case GEMM_F1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
         case GEMM_F2:
+            if (as) return launch_gemm_as<true, true, false>(K_GEMM_F2, a, s);
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, true, true, false, 8, false, 4>(K_GEMM_F2, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, true, true, false, 8, false, 4>(K_GEMM_F2, a, s);
         case GEMM_F2_NOTAPE:
+            if (as) return launch_gemm_as<false, true, false>(K_GEMM_F2, a, s);
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, false, 8, false, 4>(K_GEMM_F2, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, false, 8, false, 4>(K_GEMM_F2, a, s);
         case GEMM_DH:
@@ -787,6 +1025,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s);
         case GEMM_B1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
         case GEMM_B2:
+            if (as) return launch_gemm_as<false, true, true>(K_GEMM_B2, a, s);
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s);
         case GEMM_PLANE: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4, true>(K_GEMM_PLANE, a, s);
