@@ -806,13 +806,25 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
 
     // Stage the block: chunk i (float4) of the 64 x K block is row i / (K/4),
     // columns 4 (i % (K/4)); rows past M read row M-1 (never stored or summed).
+    // The column scales of the epilogue (OUT2) for every tile, first.
+    float c2all[TPW][FN];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            c2all[tt][j] = OUT2 ? p.out2col[(t0 + tt) * AS_BN + wn * TN + j * 32 + (lane & 31)] : 0.0f;
     {
+        // all of a thread's chunks in flight at once (up to 32 float4); when
+        // 256 is a multiple of the chunks per row, a thread's chunks share
+        // one column group and its scales are loaded once
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)M * p.lda * 4);
         const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.colscale, (uint64_t)K * 4);
         constexpr int cpr = K / 4, nch = AS_BM * cpr;  // chunks per row, in the block
-        constexpr int UNR = 8;
+        constexpr int UNR = nch / 256 < 32 ? nch / 256 : 32;
+        constexpr bool onecol = 256 % cpr == 0;
+        const f32x4_t c1 = onecol ? load_f32x4(rC, (uint32_t)(16 * (tid % cpr)), 0u) : f32x4_t{};
         for (int i0 = 0; i0 < nch; i0 += 256 * UNR) {
-            f32x4_t v[UNR], c[UNR];
+            f32x4_t v[UNR], c[onecol ? 1 : UNR];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 const int i = i0 + u * 256 + tid;
@@ -821,14 +833,14 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
                 int64_t gm = m0 + row;
                 gm = gm < M ? gm : M - 1;
                 v[u] = load_f32x4(rA, (uint32_t)((gm * p.lda + 4 * c4) * 4), 0u);
-                c[u] = load_f32x4(rC, (uint32_t)(16 * c4), 0u);
+                if (!onecol) c[u] = load_f32x4(rC, (uint32_t)(16 * c4), 0u);
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 const int i = i0 + u * 256 + tid;
                 if (i < nch) {
                     const int row = i / cpr, c4 = i - row * cpr;
-                    const f32x4_t cs = c[u] * p.ascale;
+                    const f32x4_t cs = (onecol ? c1 : c[onecol ? 0 : u]) * p.ascale;
                     uint2 h;
                     h.x = f16x2_scaled(v[u].x, cs.x, v[u].y, cs.y);
                     h.y = f16x2_scaled(v[u].z, cs.z, v[u].w, cs.w);
@@ -858,6 +870,32 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
     for (int tt = 0; tt < TPW; ++tt) {
         const int t = t0 + tt;
         if (tt + 1 < TPW) AS_WLOAD(tt + 1);
+        // epilogue addressing: element (i, v, j) at row rl + 32 i + 8 (v/4) +
+        // v%4, column cb + 32 j; the row stride is re-read per tile (opaque
+        // to the compiler), so its uniform offsets are formed per tile
+        // rather than held across tiles
+        int Nl = N;
+        asm volatile("" : "+s"(Nl));
+        const int cb = t * AS_BN + wn * TN + (lane & 31);
+        const uint32_t loff = (uint32_t)((rl * Nl + cb) * 4);
+#define AS_UOFF(i, v, j) ((uint32_t)((8 * ((v) >> 2) + ((v) & 3)) * Ni + (j) * 32) * 4u)
+        // the dot operand of the epilogue (DOT), loaded before the MFMAs so
+        // its latency is hidden behind them
+        float oth[DOT ? FM : 1][DOT ? FN : 1][DOT ? 16 : 1];
+        if (DOT) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                int Ni = Nl;
+                asm volatile("" : "+s"(Ni));
+                const uint32_t lo_ = loff + (uint32_t)(i * 32 * Ni * 4);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const bool in_ = full || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) oth[i][j][v] = in_ ? load_f32_nt(rD, lo_, AS_UOFF(i, v, j)) : 0.0f;
+                }
+            }
+        }
         f32x16_t acc[FM][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -898,20 +936,9 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
             __builtin_amdgcn_sched_barrier(0);
         }
 #undef AS_FRAGS
-        // epilogue: element (i, v, j) at row rl + 32 i + 8 (v/4) + v%4, column cb + 32 j;
-        // the row stride is re-read per tile (opaque to the compiler), so its
-        // 64 uniform offsets are formed here rather than held across tiles
-        int Nl = N;
-        asm volatile("" : "+s"(Nl));
-        const int cb = t * AS_BN + wn * TN + (lane & 31);
-        const uint32_t loff = (uint32_t)((rl * Nl + cb) * 4);
-        float c2[FN], dsum[FN];
+        float dsum[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            c2[j] = OUT2 ? p.out2col[cb + j * 32] : 0.0f;
-            dsum[j] = 0.0f;
-        }
-#define AS_UOFF(i, v, j) ((uint32_t)((8 * ((v) >> 2) + ((v) & 3)) * Ni + (j) * 32) * 4u)
+        for (int j = 0; j < FN; ++j) dsum[j] = 0.0f;
 #define AS_EPI(GUARD)                                                                      \
         do {                                                                               \
             _Pragma("unroll") for (int i = 0; i < FM; ++i) {                               \
@@ -919,21 +946,19 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
                 int Ni = Nl;                                                               \
                 asm volatile("" : "+s"(Ni));                                               \
                 const uint32_t lo_ = loff + (uint32_t)(i * 32 * Ni * 4);                   \
-                float oth[DOT ? FN : 1][DOT ? 16 : 1], old[OUT2 ? FN : 1][OUT2 ? 16 : 1];  \
+                float old[OUT2 ? FN : 1][OUT2 ? 16 : 1];                                   \
                 _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
                     const bool in_ = !(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M; \
-                    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                       \
-                        if (DOT) oth[j][v] = in_ ? load_f32_nt(rD, lo_, AS_UOFF(i, v, j)) : 0.0f; \
+                    _Pragma("unroll") for (int j = 0; j < FN; ++j)                         \
                         if (OUT2) old[j][v] = (p.out2acc && in_) ? load_f32(rO2, lo_, AS_UOFF(i, v, j)) : 0.0f; \
-                    }                                                                      \
                 }                                                                          \
                 _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
                     if (!(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M) {            \
                         _Pragma("unroll") for (int j = 0; j < FN; ++j) {                   \
                             const float val = acc[i][j][v] * osc;                          \
                             if (OUT) store_f32(rO, lo_, AS_UOFF(i, v, j), val);           \
-                            if (OUT2) store_f32_nt(rO2, lo_, AS_UOFF(i, v, j), old[j][v] + val * c2[j]); \
-                            if (DOT) dsum[j] += val * oth[j][v];                           \
+                            if (OUT2) store_f32_nt(rO2, lo_, AS_UOFF(i, v, j), old[j][v] + val * c2all[tt][j]); \
+                            if (DOT) dsum[j] += val * oth[i][j][v];                        \
                         }                                                                  \
                     }                                                                      \
                 }                                                                          \
