@@ -1081,7 +1081,12 @@ constexpr int TN_BM = 128, TN_BN = 128, TN_LDK = 40;
 __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
     __shared__ __attribute__((aligned(16))) _Float16 As[2][TN_BM * TN_LDK];
     __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TN_BN * TN_LDK];
-    int b = blockIdx.x, j = 0;
+    // consecutive tiles (the N tiles of an M tile first) on one XCD: its
+    // workgroups share their A columns and the B operand in its L2
+    const int G = gridDim.x;
+    int b = (G % NUM_XCD == 0) ? (int)(blockIdx.x % NUM_XCD) * (G / NUM_XCD) + (int)(blockIdx.x / NUM_XCD)
+                               : (int)blockIdx.x;
+    int j = 0;
     if (jobs.count > 1 && b >= jobs.job[1].tiles_before) j = 1;
     const TnJob &jb = jobs.job[j];
     b -= jb.tiles_before;
