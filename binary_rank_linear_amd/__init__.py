@@ -51,6 +51,13 @@ def load():
     lib.blr_backward_signs.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, f32, p, p, p, p, i32, p, p, i32,
                                        p, sz, p]
     lib.blr_backward_signs.restype = i32
+    lib.blr_workspace_bytes_paths.argtypes = [i64, i64, i64, i64, i64]
+    lib.blr_workspace_bytes_paths.restype = sz
+    lib.blr_forward_paths.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, p, p, i32, p, p, sz, p]
+    lib.blr_forward_paths.restype = i32
+    lib.blr_backward_paths.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p, f32, p, p, p, p, i32, p, p,
+                                       i32, p, sz, p]
+    lib.blr_backward_paths.restype = i32
     lib.blr_plane_linear.argtypes = [i64, i64, i64, p, p, p, f32, p]
     lib.blr_plane_linear.restype = i32
     lib.blr_sumsq.argtypes = [p, i64, p, i32, p]
@@ -238,6 +245,83 @@ def blr_backward_signs(x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale: f
                                      _ptr(grad_v), int(bool(accumulate_signs)), _ptr(ws), ws.numel(),
                                      _stream(stream)), "blr_backward_signs")
     return dh, dl, dg, dx, grad_u, grad_v
+
+
+def blr_workspace_bytes_paths(M: int, d_in: int, d_out: int, r: int, paths: int) -> int:
+    return int(load().blr_workspace_bytes_paths(M, d_in, d_out, r, paths))
+
+
+def _paths_shapes(x, bits_u, bits_v, h, l, g):
+    import torch
+    f32 = (torch.float32,)
+    M, d_in = _need(x, "x", f32).shape
+    P, d_out = _need(h, "h", f32).shape
+    r = _need(l, "l", f32, (P, l.shape[1])).shape[1]
+    _need(g, "g", f32, (P, d_in))
+    W = (r + 31) // 32
+    _need(bits_u, "bits_u", _bits_dtypes(), (P, d_out, W))
+    _need(bits_v, "bits_v", _bits_dtypes(), (P, d_in, W))
+    return M, d_in, d_out, r, P
+
+
+def blr_forward_paths(x, bits_u, bits_v, h, l, g, *, y=None, accumulate_y=False, tape_a=None, ws=None, stream=None):
+    """Forward of a layer of P paths, fused: bits_u [P][d_out][W], bits_v
+    [P][d_in][W], h [P][d_out], l [P][r], g [P][d_in]. y (+)= sum_p h_p.c_p;
+    the a tape is [M][P r]. Returns (y, tape_a)."""
+    import torch
+    f32 = (torch.float32,)
+    M, d_in, d_out, r, P = _paths_shapes(x, bits_u, bits_v, h, l, g)
+    dev = x.device
+    y = torch.empty((M, d_out), dtype=torch.float32, device=dev) if y is None else _need(y, "y", f32, (M, d_out))
+    tape_a = torch.empty((M, P * r), dtype=torch.float32, device=dev) if tape_a is None else \
+        _need(tape_a, "tape_a", f32, (M, P * r))
+    if ws is None:
+        ws = workspace_paths(M, d_in, d_out, r, P, dev)
+    _check(load().blr_forward_paths(M, d_in, d_out, r, P, _ptr(x), _ptr(bits_u), _ptr(bits_v), _ptr(h), _ptr(l),
+                                    _ptr(g), _ptr(y), int(bool(accumulate_y)), _ptr(tape_a), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "blr_forward_paths")
+    return y, tape_a
+
+
+def blr_backward_paths(x, dy, bits_u, bits_v, h, l, g, tape_a, gscale: float, *, dh=None, dl=None, dg=None, dx=None,
+                       accumulate_dx=False, signs=False, grad_u=None, grad_v=None, accumulate_signs=False, ws=None,
+                       stream=None):
+    """Backward of a layer of P paths (blr_forward_paths' tape). dh [P][d_out],
+    dl [P][r], dg [P][d_in] accumulate (zeros when not given); dx is
+    overwritten unless accumulate_dx. With signs (or grad_u / grad_v given)
+    also the sign gradients [P][d_out][r] and [P][d_in][r]. Returns
+    (dh, dl, dg, dx, grad_u, grad_v), the last two None without signs."""
+    import torch
+    f32 = (torch.float32,)
+    M, d_in, d_out, r, P = _paths_shapes(x, bits_u, bits_v, h, l, g)
+    _need(dy, "dy", f32, (M, d_out))
+    _need(tape_a, "tape_a", f32, (M, P * r))
+    dev = x.device
+    dh = torch.zeros((P, d_out), dtype=torch.float32, device=dev) if dh is None else _need(dh, "dh", f32, (P, d_out))
+    dl = torch.zeros((P, r), dtype=torch.float32, device=dev) if dl is None else _need(dl, "dl", f32, (P, r))
+    dg = torch.zeros((P, d_in), dtype=torch.float32, device=dev) if dg is None else _need(dg, "dg", f32, (P, d_in))
+    dx = torch.empty((M, d_in), dtype=torch.float32, device=dev) if dx is None else _need(dx, "dx", f32, (M, d_in))
+    if signs or grad_u is not None or grad_v is not None:
+        grad_u = torch.empty((P, d_out, r), dtype=torch.float32, device=dev) if grad_u is None else \
+            _need(grad_u, "grad_u", f32, (P, d_out, r))
+        grad_v = torch.empty((P, d_in, r), dtype=torch.float32, device=dev) if grad_v is None else \
+            _need(grad_v, "grad_v", f32, (P, d_in, r))
+    if ws is None:
+        ws = workspace_paths(M, d_in, d_out, r, P, dev)
+    _check(load().blr_backward_paths(M, d_in, d_out, r, P, _ptr(x), _ptr(dy), _ptr(bits_u), _ptr(bits_v), _ptr(h),
+                                     _ptr(l), _ptr(g), _ptr(tape_a), ctypes.c_float(gscale), _ptr(dh), _ptr(dl),
+                                     _ptr(dg), _ptr(dx), int(bool(accumulate_dx)), _ptr(grad_u), _ptr(grad_v),
+                                     int(bool(accumulate_signs)), _ptr(ws), ws.numel(), _stream(stream)),
+           "blr_backward_paths")
+    return dh, dl, dg, dx, grad_u, grad_v
+
+
+def workspace_paths(M: int, d_in: int, d_out: int, r: int, paths: int, device=None):
+    import torch
+    n = blr_workspace_bytes_paths(M, d_in, d_out, r, paths)
+    if n == 0:
+        raise BlrError(-2, "blr_workspace_bytes_paths")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
 def blr_plane_linear(x, plane, scale: float = 1.0, *, y=None, stream=None):

@@ -59,31 +59,32 @@ constexpr size_t ALIGN = 256;
 size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bits_t;  // transposed bitmap [r][max(d_in, d_out)/32] (u32)
-    size_t db;      // f32 [M][r]
+    size_t bits_t;  // transposed bitmaps [P][r][max(d_in, d_out)/32] (u32)
+    size_t db;      // f32 [M][P r]
     size_t part_h, part_l, part_g;
     size_t total;
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+// P paths (1 for a plain layer); the paths' ranks lie side by side.
+Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P = 1) {
     Layout L;
     size_t off = 0;
     L.bits_t = off;
-    off += up((size_t)(r * ((d_in > d_out ? d_in : d_out) / 32)) * 4);
+    off += up((size_t)(P * r * ((d_in > d_out ? d_in : d_out) / 32)) * 4);
     L.db = off;
-    off += up((size_t)(M * r) * 4);
-    // dh partials: 2 * ceil(M/64) rows (>= ceil(M/32)) cover every producer
-    // (the c-tape column sum, the recomputed-c contraction, B1 with dh fused
-    // on 32-token tiles or on 64-token tiles of two rank halves); dl
-    // partials: one row per 32 tokens
+    off += up((size_t)(M * P * r) * 4);
+    // dh partials: 2 * ceil(M/64) rows per path (>= ceil(M/32)) cover every
+    // producer (the c-tape column sum, the recomputed-c contraction, B1 with
+    // dh fused on 64-token tiles of up to two rank halves); dl partials: one
+    // row per 32 tokens; dg partials: one row per 64 tokens and path
     L.part_h = off;
-    off += up((size_t)(2 * ceil_div(M, GEMM_BM_MIN) * d_out) * 4);
+    off += up((size_t)(2 * P * ceil_div(M, GEMM_BM_MIN) * d_out) * 4);
     L.part_l = off;
-    off += up((size_t)(ceil_div(M, PART_ROWS_MIN) * r) * 4);
+    off += up((size_t)(ceil_div(M, PART_ROWS_MIN) * P * r) * 4);
     L.part_g = off;
-    off += up((size_t)(ceil_div(M, GEMM_BM_MIN) * d_in) * 4);
+    off += up((size_t)(P * ceil_div(M, GEMM_BM_MIN) * d_in) * 4);
     L.total = off;
     return L;
 }
@@ -91,7 +92,12 @@ Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
 // Sizes the kernels accept: d_in, d_out, r multiples of 128 (the page's GEMM
 // contract), M >= 1, and everything small enough for 32-bit grid and column
 // indices.
-bool shape_ok(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+bool shape_ok(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P = 1) {
+    if (P < 1 || P > MAX_PATHS) return false;
+    if (P > 1) {
+        // the paths' ranks side by side are one operand dimension
+        if (!shape_ok(M, d_in, d_out, P * r)) return false;
+    }
     if (M < 1 || d_in < 128 || d_out < 128 || r < 128) return false;
     if (d_in % 128 || d_out % 128 || r % 128) return false;
     const int64_t LIM = (int64_t)1 << 24;  // ranks
@@ -178,12 +184,19 @@ int blr_expand_signs(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl
     return launch_expand(jobs, (hipStream_t)stream) == hipSuccess ? BLR_OK : BLR_ERR_HIP;
 }
 
-int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
-                const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y, int accumulate_y,
-                float *tape_a, float *tape_c, void *workspace, size_t workspace_bytes, void *stream) {
+// A layer of P paths (P = 1: the plain layer). Path p's operands are the
+// p-th blocks of bits_u [P][d_out][r/32], bits_v [P][d_in][r/32],
+// h [P][d_out], l [P][r], g [P][d_in]; the a tape is [M][P r] (the paths'
+// ranks side by side). F1 runs once over the concatenated ranks; F2 runs
+// once with the paths along K (one flush per path) when P > 1.
+static int forward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P, const float *x,
+                        const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                        const float *g, float *y, int accumulate_y, float *tape_a, float *tape_c, void *workspace,
+                        size_t workspace_bytes, void *stream) {
     if (!x || !bits_u || !bits_v || !h || !l || !g || !y || !tape_a) return BLR_ERR_NULL;
-    if (!shape_ok(M, d_in, d_out, r)) return BLR_ERR_SHAPE;
-    const Layout L = layout(M, d_in, d_out, r);
+    if (!shape_ok(M, d_in, d_out, r, P)) return BLR_ERR_SHAPE;
+    if (P > 1 && tape_c) return BLR_ERR_SHAPE;  // no c tape for several paths
+    const Layout L = layout(M, d_in, d_out, r, P);
     if (workspace == nullptr || workspace_bytes < L.total) return BLR_ERR_WORKSPACE;
     const void *f16a[] = {x, h, l, g, y, tape_a, tape_c ? tape_c : tape_a, workspace};
     for (const void *p : f16a)
@@ -194,8 +207,8 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
 
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
-    uint32_t *bits_vt = (uint32_t *)(ws + L.bits_t);  // S_V^T as a bitmap [r][d_in/32]
-    BLR_TRY(launch_transpose_bits(bits_v, d_in, r, bits_vt, s));
+    uint32_t *bits_vt = (uint32_t *)(ws + L.bits_t);  // S_V^T per path, [P][r][d_in/32]
+    BLR_TRY(launch_transpose_bits(bits_v, d_in, r, bits_vt, s, (int)P));
 
     GemmArgs f1 = {};
     f1.A = x;
@@ -204,44 +217,77 @@ int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *
     f1.ascale = 1.0f;
     f1.Bbits = bits_vt;
     f1.M = M;
-    f1.N = (int)r;
+    f1.N = (int)(P * r);
     f1.K = (int)d_in;
     f1.oscale = 1.0f;
     f1.out = tape_a;
+    if (P > 1) {
+        f1.path_n = (int)r;      // path n0 / r: x staged with g_p
+        f1.cs_pstride = d_in;
+    }
     BLR_TRY(launch_gemm(GEMM_F1, f1, s));
 
     GemmArgs f2 = {};
     f2.A = tape_a;
-    f2.lda = r;
+    f2.lda = P * r;
     f2.colscale = l;
     f2.ascale = 1.0f;
     f2.Bbits = bits_u;
     f2.M = M;
     f2.N = (int)d_out;
-    f2.K = (int)r;
+    f2.K = (int)(P * r);
     f2.oscale = 1.0f;
     f2.out = tape_c;
     f2.out2 = y;
     f2.out2col = h;
     f2.out2acc = accumulate_y ? 1 : 0;
-    BLR_TRY(launch_gemm(tape_c ? GEMM_F2 : GEMM_F2_NOTAPE, f2, s));
+    if (P > 1) {
+        f2.path_k = (int)r;                 // S_U of path q: bits_u + q d_out r/32 words
+        f2.b_pstride = d_out * (r / 32);
+        f2.o2_pstride = d_out;              // h_q
+        BLR_TRY(launch_gemm(GEMM_F2_MP, f2, s));
+    } else {
+        BLR_TRY(launch_gemm(tape_c ? GEMM_F2 : GEMM_F2_NOTAPE, f2, s));
+    }
     return BLR_OK;
 }
 
-// The backward, and with grad_u / grad_v the sign gradients after it (both
-// or neither).
-static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
-                         const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
-                         const float *g, const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl,
-                         float *dg, float *dx, int accumulate_dx, float *grad_u, float *grad_v, int accumulate_signs,
-                         void *workspace, size_t workspace_bytes, void *stream) {
+int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
+                const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y, int accumulate_y,
+                float *tape_a, float *tape_c, void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_impl(M, d_in, d_out, r, 1, x, bits_u, bits_v, h, l, g, y, accumulate_y, tape_a, tape_c, workspace,
+                        workspace_bytes, stream);
+}
+
+int blr_forward_paths(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t paths, const float *x,
+                      const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                      float *y, int accumulate_y, float *tape_a, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    return forward_impl(M, d_in, d_out, r, paths, x, bits_u, bits_v, h, l, g, y, accumulate_y, tape_a, nullptr,
+                        workspace, workspace_bytes, stream);
+}
+
+size_t blr_workspace_bytes_paths(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t paths) {
+    if (!shape_ok(M, d_in, d_out, r, paths)) return 0;
+    return layout(M, d_in, d_out, r, paths).total;
+}
+
+// The backward of P paths, and with grad_u / grad_v the sign gradients
+// after it (both or neither). dh [P][d_out], dl [P][r], dg [P][d_in],
+// grad_u [P][d_out][r], grad_v [P][d_in][r].
+static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P, const float *x,
+                         const float *dy, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
+                         const float *l, const float *g, const float *tape_a, const float *tape_c, float gscale,
+                         float *dh, float *dl, float *dg, float *dx, int accumulate_dx, float *grad_u, float *grad_v,
+                         int accumulate_signs, void *workspace, size_t workspace_bytes, void *stream) {
     if (!x || !dy || !bits_u || !bits_v || !h || !l || !g || !tape_a || !dh || !dl || !dg || !dx)
         return BLR_ERR_NULL;
     if ((grad_u == nullptr) != (grad_v == nullptr)) return BLR_ERR_NULL;
     if (grad_u && (!aligned16(grad_u) || !aligned16(grad_v))) return BLR_ERR_ALIGN;
-    if (!shape_ok(M, d_in, d_out, r)) return BLR_ERR_SHAPE;
+    if (!shape_ok(M, d_in, d_out, r, P)) return BLR_ERR_SHAPE;
+    if (P > 1 && tape_c) return BLR_ERR_SHAPE;
     if (!pow2_scale_ok(gscale)) return BLR_ERR_SCALE;
-    const Layout L = layout(M, d_in, d_out, r);
+    const Layout L = layout(M, d_in, d_out, r, P);
     if (workspace == nullptr || workspace_bytes < L.total) return BLR_ERR_WORKSPACE;
     const void *f16a[] = {x, dy, h, l, g, tape_a, tape_c ? tape_c : tape_a, dh, dl, dg, dx, workspace};
     for (const void *p : f16a)
@@ -252,45 +298,48 @@ static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, cons
 
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
-    uint32_t *bits_ut = (uint32_t *)(ws + L.bits_t);  // S_U^T as a bitmap [r][d_out/32]
-    float *db = (float *)(ws + L.db);
+    uint32_t *bits_ut = (uint32_t *)(ws + L.bits_t);  // S_U^T per path, [P][r][d_out/32]
+    float *db = (float *)(ws + L.db);                 // [M][P r]
     float *part_h = (float *)(ws + L.part_h);
     float *part_l = (float *)(ws + L.part_l);
     float *part_g = (float *)(ws + L.part_g);
     const float inv = 1.0f / gscale;  // exact: gscale is a power of two
+    const int64_t Pr = P * r;
     const bool fused = tape_c == nullptr && b1dh_cols(r) > 0;  // B1 with dh fused
     const int64_t mt_b1 = ceil_div(M, fused ? b1dh_tile_rows(r) : gemm_tile_rows(GEMM_B1));
-    const int64_t mt_b2 = ceil_div(M, gemm_tile_rows(GEMM_B2));
+    const int64_t mt_b2 = ceil_div(M, gemm_tile_rows(P > 1 ? GEMM_B2_MP : GEMM_B2));
 
-    BLR_TRY(launch_transpose_bits(bits_u, d_out, r, bits_ut, s));
+    BLR_TRY(launch_transpose_bits(bits_u, d_out, r, bits_ut, s, (int)P));
 
-    // partials of dh = sum_t dy.c: from the stored tape, or with c
-    // recomputed by F2's contraction (same tiles, so the same c)
-    int64_t nparts_h = mt_b1;
+    // partials of dh_p = sum_t dy.c_p, nparts_h rows per path: inside B1
+    // below, from the stored tape, or with c recomputed by F2's contraction
+    // (same tiles, so the same c)
+    int64_t nparts_h = 0;
     if (fused) {
-        // computed inside B1 below, one partial row per (row tile, rank tile)
-        nparts_h = mt_b1 * (r / b1dh_cols(r));
+        nparts_h = mt_b1 * (r / b1dh_cols(r));  // one row per (rank tile, row tile) of the path
     } else if (tape_c) {
         BLR_TRY(launch_colsum(dy, tape_c, M, (int)d_out, part_h, s));
         nparts_h = ceil_div(M, COLSUM_ROWS);
     } else {
-        GemmArgs rc = {};
-        rc.A = tape_a;
-        rc.lda = r;
-        rc.colscale = l;
-        rc.ascale = 1.0f;
-        rc.Bbits = bits_u;
-        rc.M = M;
-        rc.N = (int)d_out;
-        rc.K = (int)r;
-        rc.oscale = 1.0f;
-        rc.dot_other = dy;
-        rc.dot_partial = part_h;
-        BLR_TRY(launch_gemm(GEMM_DH, rc, s));
         nparts_h = ceil_div(M, gemm_tile_rows(GEMM_DH));
+        for (int64_t q = 0; q < P; ++q) {
+            GemmArgs rc = {};
+            rc.A = tape_a + q * r;
+            rc.lda = Pr;
+            rc.colscale = l + q * r;
+            rc.ascale = 1.0f;
+            rc.Bbits = bits_u + q * d_out * (r / 32);
+            rc.M = M;
+            rc.N = (int)d_out;
+            rc.K = (int)r;
+            rc.oscale = 1.0f;
+            rc.dot_other = dy;
+            rc.dot_partial = part_h + q * nparts_h * d_out;
+            BLR_TRY(launch_gemm(GEMM_DH, rc, s));
+        }
     }
 
-    // db = f16(dy.h.gs) S_U / gs; dl += sum_t a.db
+    // db_p = f16(dy.h_p.gs) S_U,p / gs for all paths side by side; dl += sum_t a.db
     GemmArgs b1 = {};
     b1.A = dy;
     b1.lda = d_out;
@@ -298,58 +347,82 @@ static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, cons
     b1.ascale = gscale;
     b1.Bbits = bits_ut;
     b1.M = M;
-    b1.N = (int)r;
+    b1.N = (int)Pr;
     b1.K = (int)d_out;
     b1.oscale = inv;
     b1.out = db;
     b1.dot_other = tape_a;
     b1.dot_partial = part_l;
+    if (P > 1) {
+        b1.path_n = (int)r;  // path n0 / r: dy staged with h_p
+        b1.cs_pstride = d_out;
+    }
     if (fused) {
-        // and, per 32-column block of dy, c = f16(a.l) S_U^T recomputed and
-        // dh partials sum_t dy.c (c is not stored)
+        // and, per 32-column block of dy, c_p = f16(a_p.l_p) S_U,p^T recomputed
+        // and dh partials sum_t dy.c_p (c is not stored)
         b1.dh_bits = bits_u;
         b1.dh_a = tape_a;
         b1.dh_l = l;
         b1.dh_partial = part_h;
+        if (P > 1) {
+            b1.dh_pstride = d_out * (r / 32);
+            b1.dh_row_words = (int)(r / 32);
+        }
         BLR_TRY(launch_gemm(GEMM_B1_DH, b1, s));
     } else {
         BLR_TRY(launch_gemm(GEMM_B1, b1, s));
     }
 
-    // dx' = f16(db.l.gs) S_V^T / gs; dx (+)= g.dx'; dg += sum_t x.dx'
+    // dx'_p = f16(db_p.l_p.gs) S_V,p^T / gs; dx (+)= sum_p g_p.dx'_p;
+    // dg_p += sum_t x.dx'_p
     GemmArgs b2 = {};
     b2.A = db;
-    b2.lda = r;
+    b2.lda = Pr;
     b2.colscale = l;
     b2.ascale = gscale;
     b2.Bbits = bits_v;
     b2.M = M;
     b2.N = (int)d_in;
-    b2.K = (int)r;
+    b2.K = (int)Pr;
     b2.oscale = inv;
     b2.out2 = dx;
     b2.out2col = g;
     b2.out2acc = accumulate_dx ? 1 : 0;
     b2.dot_other = x;
     b2.dot_partial = part_g;
-    BLR_TRY(launch_gemm(GEMM_B2, b2, s));
+    if (P > 1) {
+        b2.path_k = (int)r;
+        b2.b_pstride = d_in * (r / 32);
+        b2.o2_pstride = d_in;
+        b2.dot_pstride = mt_b2 * d_in;
+        BLR_TRY(launch_gemm(GEMM_B2_MP, b2, s));
+    } else {
+        BLR_TRY(launch_gemm(GEMM_B2, b2, s));
+    }
 
-    // dh, dl, dg += their partial sums, one launch
+    // dh_p, dl, dg_p += their partial sums, one launch
     FinishJobs fin = {};
-    fin.job[0] = {part_h, nparts_h, (int)d_out, dh};
-    fin.job[1] = {part_l, mt_b1, (int)r, dl};
-    fin.job[2] = {part_g, mt_b2, (int)d_in, dg};
-    fin.count = 3;
+    int nj = 0;
+    for (int64_t q = 0; q < P; ++q) fin.job[nj++] = {part_h + q * nparts_h * d_out, nparts_h, (int)d_out, dh + q * d_out};
+    fin.job[nj++] = {part_l, mt_b1, (int)Pr, dl};
+    for (int64_t q = 0; q < P; ++q) fin.job[nj++] = {part_g + q * mt_b2 * d_in, mt_b2, (int)d_in, dg + q * d_in};
+    fin.count = nj;
     BLR_TRY(launch_finish(fin, s));
 
     if (grad_u) {
-        // G_U = diag(h) dy^T a diag(l) from f16(dy.h.gs) and f16(a.l);
-        // G_V = diag(g) x^T db diag(l) from f16(x.g) and f16(db.l.gs); both / gs
+        // G_U,p = diag(h_p) dy^T a_p diag(l_p) from f16(dy.h_p.gs) and
+        // f16(a_p.l_p); G_V,p = diag(g_p) x^T db_p diag(l_p) from f16(x.g_p)
+        // and f16(db_p.l_p.gs); both / gs. The a tape and db hold the paths
+        // side by side, so path p's columns start at p r with row stride P r.
         TnJobs tj = {};
         tj.T = M;
-        tj.count = 2;
-        tj.job[0] = {dy, h, gscale, tape_a, l, 1.0f, (int)d_out, (int)r, inv, grad_u, accumulate_signs ? 1 : 0, 0};
-        tj.job[1] = {x, g, 1.0f, db, l, gscale, (int)d_in, (int)r, inv, grad_v, accumulate_signs ? 1 : 0, 0};
+        tj.count = 0;
+        for (int64_t q = 0; q < P; ++q) {
+            tj.job[tj.count++] = {dy, h + q * d_out, gscale, tape_a + q * r, l + q * r, 1.0f, (int)d_out, (int)r, inv,
+                                  grad_u + q * d_out * r, accumulate_signs ? 1 : 0, 0, d_out, Pr};
+            tj.job[tj.count++] = {x, g + q * d_in, 1.0f, db + q * r, l + q * r, gscale, (int)d_in, (int)r, inv,
+                                  grad_v + q * d_in * r, accumulate_signs ? 1 : 0, 0, d_in, Pr};
+        }
         BLR_TRY(launch_gemm_tn(tj, s));
     }
     return BLR_OK;
@@ -359,8 +432,8 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
                  const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
                  const float *tape_a, const float *tape_c, float gscale, float *dh, float *dl, float *dg, float *dx,
                  int accumulate_dx, void *workspace, size_t workspace_bytes, void *stream) {
-    return backward_impl(M, d_in, d_out, r, x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale, dh, dl, dg, dx,
-                         accumulate_dx, nullptr, nullptr, 0, workspace, workspace_bytes, stream);
+    return backward_impl(M, d_in, d_out, r, 1, x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale, dh, dl, dg,
+                         dx, accumulate_dx, nullptr, nullptr, 0, workspace, workspace_bytes, stream);
 }
 
 int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
@@ -369,8 +442,17 @@ int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const 
                        float *dx, int accumulate_dx, float *grad_u, float *grad_v, int accumulate_signs,
                        void *workspace, size_t workspace_bytes, void *stream) {
     if (!grad_u || !grad_v) return BLR_ERR_NULL;
-    return backward_impl(M, d_in, d_out, r, x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale, dh, dl, dg, dx,
-                         accumulate_dx, grad_u, grad_v, accumulate_signs, workspace, workspace_bytes, stream);
+    return backward_impl(M, d_in, d_out, r, 1, x, dy, bits_u, bits_v, h, l, g, tape_a, tape_c, gscale, dh, dl, dg,
+                         dx, accumulate_dx, grad_u, grad_v, accumulate_signs, workspace, workspace_bytes, stream);
+}
+
+int blr_backward_paths(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t paths, const float *x,
+                       const float *dy, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
+                       const float *l, const float *g, const float *tape_a, float gscale, float *dh, float *dl,
+                       float *dg, float *dx, int accumulate_dx, float *grad_u, float *grad_v, int accumulate_signs,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    return backward_impl(M, d_in, d_out, r, paths, x, dy, bits_u, bits_v, h, l, g, tape_a, nullptr, gscale, dh, dl,
+                         dg, dx, accumulate_dx, grad_u, grad_v, accumulate_signs, workspace, workspace_bytes, stream);
 }
 
 int blr_plane_linear(int64_t M, int64_t n, int64_t k, const float *x, const uint16_t *plane, float *y, float scale,

@@ -61,12 +61,34 @@ struct GemmArgs {
     const uint32_t *dh_bits; // bitmap of S_U [K][N/32] (K = d_out, N = r)
     const float *dh_a;       // the a tape [M][N]
     const float *dh_l;       // l [N]
-    float *dh_partial;       // [ceil(M/BM) * (N/BN)][K]
+    float *dh_partial;       // [(N/BN) * ceil(M/BM)][K], row nt * ceil(M/BM) + mt
+    // A layer of several paths (y = sum_p h_p . c_p); zero for one path.
+    // Paths along N (F1, B1: the ranks of all paths side by side): path_n
+    // columns per path; the tile of column n0 belongs to path n0 / path_n,
+    // whose column scales start at colscale + path * cs_pstride and, for the
+    // fused dh role, whose S_U bitmap is dh_bits + path * dh_pstride words
+    // with dh_row_words words per row.
+    int path_n;
+    int64_t cs_pstride, dh_pstride;
+    int dh_row_words;
+    // Paths along K (GEMM_F2_MP, GEMM_B2_MP: K = paths * path_k): the
+    // bitmap of path q is Bbits + q * b_pstride words, rows of path_k / 32
+    // words; at the end of each path's ranks the product is scaled by
+    // out2col + q * o2_pstride into a running sum (stored at the end), and
+    // that path's column partials go to dot_partial + q * dot_pstride.
+    int path_k;
+    int64_t b_pstride, o2_pstride, dot_pstride;
 };
 
 // F2 writes the c tape and y (F2) or y only (F2_NOTAPE); DH repeats F2's
 // contraction with the same tiles (so c is bit-identical) and sums dy.c.
-enum GemmKind { GEMM_F1 = 0, GEMM_F2, GEMM_F2_NOTAPE, GEMM_B1, GEMM_B2, GEMM_DH, GEMM_B1_DH, GEMM_PLANE };
+enum GemmKind {
+    GEMM_F1 = 0, GEMM_F2, GEMM_F2_NOTAPE, GEMM_B1, GEMM_B2, GEMM_DH, GEMM_B1_DH, GEMM_PLANE,
+    GEMM_F2_MP,  // y (+)= sum_p h_p . c_p over paths along K (no c tape)
+    GEMM_B2_MP   // dx (+)= sum_p g_p . dx'_p, partials of dg_p per path
+};
+// Most paths of one layer the fused launches serve.
+constexpr int MAX_PATHS = 4;
 // GEMM_B1_DH tiles: rank columns and token rows per workgroup (0 where the
 // fused launch does not serve r). The dh partials have
 // ceil(M / b1dh_tile_rows(r)) * (r / b1dh_cols(r)) rows, at most
@@ -94,14 +116,15 @@ struct FinishJob {
     float *out;
 };
 struct FinishJobs {
-    FinishJob job[3];
-    int blocks_before[3];
+    FinishJob job[2 * MAX_PATHS + 1];
+    int blocks_before[2 * MAX_PATHS + 1];
     int count;
 };
 
 // Token-contraction jobs for the sign gradients:
 //   out[m][n] (+)= (sum_t f16(A[t][m] acol[m] ascale) f16(B[t][n] bcol[n] bscale)) oscale
-// A [T][Mo] and B [T][No] row-major; out [Mo][No]; Mo, No multiples of 128.
+// A [T][lda] and B [T][ldb] row-major (columns Mo and No used); out
+// [Mo][No]; Mo, No multiples of 128.
 struct TnJob {
     const float *A;
     const float *acol;
@@ -114,9 +137,10 @@ struct TnJob {
     float *out;
     int acc;
     int tiles_before;  // filled by the launcher
+    int64_t lda, ldb;  // row strides of A and B (elements)
 };
 struct TnJobs {
-    TnJob job[2];
+    TnJob job[2 * MAX_PATHS];
     int count;
     int64_t T;
 };
@@ -126,8 +150,10 @@ hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s);
 hipError_t launch_sumsq(const float *a, int64_t n, float *partials, int nparts, hipStream_t s);
 hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s);
 // out [r][rows/32]: bit (i % 32) of word i / 32 in row k is rank k of row i
-// of bits [rows][r/32] (rows and r multiples of 32).
-hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, uint32_t *out, hipStream_t s);
+// of bits [rows][r/32] (rows and r multiples of 32); for paths > 1, bits
+// holds that many such bitmaps back to back and out their transposes.
+hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, uint32_t *out, hipStream_t s,
+                                 int paths = 1);
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s);
 int gemm_tile_rows(GemmKind kind);
 hipError_t launch_colsum(const float *A, const float *B, int64_t M, int N, float *partial, hipStream_t s);

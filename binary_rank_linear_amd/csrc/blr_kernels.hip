@@ -221,6 +221,8 @@ __device__ __forceinline__ half8_t sign_frag(uint32_t w, uint32_t sel, uint32_t 
 __global__ __launch_bounds__(256) void transpose_bits_kernel(const uint32_t *__restrict__ bits, int64_t rows,
                                                              int64_t r, uint32_t *__restrict__ out) {
     const int64_t W = r / 32, rw = rows / 32;
+    bits += (int64_t)blockIdx.y * rows * W;  // path blockIdx.y
+    out += (int64_t)blockIdx.y * r * rw;
     const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // one wavefront per (row block, word)
     const int lane = threadIdx.x & 63;
     const int64_t nrb = (rows + 63) / 64;
@@ -241,17 +243,19 @@ __global__ __launch_bounds__(256) void transpose_bits_kernel(const uint32_t *__r
     }
 }
 
-hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, uint32_t *out, hipStream_t s) {
+hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, uint32_t *out, hipStream_t s,
+                                 int paths) {
     const int64_t waves = ((rows + 63) / 64) * (r / 32);
     prof_begin(K_TRANSPOSE, s);
-    hipLaunchKernelGGL(transpose_bits_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, bits, rows, r, out);
+    hipLaunchKernelGGL(transpose_bits_kernel, dim3((unsigned)((waves + 3) / 4), (unsigned)paths), dim3(256), 0, s,
+                       bits, rows, r, out);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
 }
 
 template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false,
-          int KB = 2, bool PLANE = false>
+          int KB = 2, bool PLANE = false, bool MP = false>
 __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kernel(GemmArgs p) {
     constexpr int NT = WM * WN * 64;  // threads of the contraction role
     constexpr int BK = 16 * KB;     // k per step: KB MFMA k-blocks, KB/2 bitmap words per plane row
@@ -270,6 +274,9 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // plane [N][K] (one 16-byte load per lane and k-block, one step ahead)
     // instead of decoded from a bitmap, and the activation has no column scale.
     static_assert(!PLANE || (!FDH && !DOT), "plane path shape");
+    // MP (paths along K): per-path flushes of the product; the column
+    // partials need every row of a column in one wave
+    static_assert(!MP || (WM == 1 && !OUT && !FDH && !PLANE), "paths along K");
     // Fused dh (B1 only): 64-token tiles, one row of waves with 64 ranks
     // each, and as many more waves in a second role (DH waves): they
     // stage the f32 dy tile and compute the dh partials, so each SIMD holds
@@ -334,7 +341,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // the loads take a 32-bit per-lane offset plus a uniform offset, so no
     // VALU address arithmetic is needed.
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)M * p.lda * 4);
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.colscale, PLANE ? 0 : (uint64_t)K * 4);
+    // paths: along N, this tile's path pn; along K, PKr ranks per path
+    const int pn = p.path_n ? n0 / p.path_n : 0;
+    const int PKr = p.path_k ? p.path_k : K;
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(p.colscale + (int64_t)pn * p.cs_pstride, PLANE ? 0 : (uint64_t)K * 4);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.Bbits, PLANE ? 0 : (uint64_t)N * K / 8);
     const __amdgpu_buffer_rsrc_t rP = make_rsrc(p.Bplane, PLANE ? (uint64_t)N * K * 2 : 0);
     const uint32_t coff = (uint32_t)c4 * 16;
@@ -345,7 +356,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 #pragma unroll
     for (int j = 0; j < FN; ++j)
         boff[j] = PLANE ? (uint32_t)(((int64_t)(n0 + wn * TN + j * 32 + (lane & 31)) * K + (lane >> 5) * 8) * 2)
-                        : (uint32_t)((int64_t)(n0 + wn * TN + j * 32 + (lane & 31)) * (K / 32) * 4);
+                        : (uint32_t)((int64_t)(n0 + wn * TN + j * 32 + (lane & 31)) * (PKr / 32) * 4);
     // v_perm selectors: byte (2s + lane group) of the word into every byte
     const uint32_t grp = (uint32_t)(lane >> 5);
     const uint32_t sel[2] = {grp * 0x01010101u, (2u + grp) * 0x01010101u};
@@ -361,7 +372,10 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // 8-byte load.
     half8_t al[FDH ? FMD * KD : 1];
     uint32_t hoff = 0;
-    const __amdgpu_buffer_rsrc_t rH = make_rsrc(p.dh_bits, FDH ? (uint64_t)K * N / 8 : 0);
+    // (paths along N: path pn's S_U, DRW words per row)
+    const int DRW = p.dh_row_words ? p.dh_row_words : N / 32;
+    const __amdgpu_buffer_rsrc_t rH =
+        make_rsrc(p.dh_bits + (int64_t)pn * p.dh_pstride, FDH ? (uint64_t)K * DRW * 4 : 0);
     if (dhw) {
 #pragma unroll
         for (int i = 0; i < FMD; ++i) {
@@ -384,7 +398,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 al[i * KD + t] = h;
             }
         }
-        hoff = (uint32_t)(((lane & 31) * (N / 32) + (n0 + wn * TN) / 32) * 4);
+        hoff = (uint32_t)(((lane & 31) * DRW + (n0 - pn * p.path_n + wn * TN) / 32) * 4);
     }
 
     f32x16_t acc[FM][FN];
@@ -412,8 +426,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 #define BLR_BLOAD(dst, grp4)                                                               \
     do {                                                                                   \
         const int g_ = (grp4) < nk / U ? (grp4) : nk / U - 1;                              \
+        /* group g_ (128 k) lies in path g_ * 128 / PKr */                                 \
+        const int pq_ = g_ * 128 / PKr;                                                    \
+        const uint32_t so_ = (uint32_t)((int64_t)pq_ * p.b_pstride * 4) + (uint32_t)(g_ - pq_ * (PKr / 128)) * 16; \
         if (!PLANE) _Pragma("unroll") for (int j = 0; j < FN; ++j) dst[j] =                \
-            load_u32x4(rB, boff[j], (uint32_t)g_ * 16);                                    \
+            load_u32x4(rB, boff[j], so_);                                                  \
     } while (0)
 
 #define BLR_SSTORE(q, buf)                                                                 \
@@ -540,7 +557,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // no more than those)
     if (dhw) {
         BLR_HLOAD(hb[0], 0u);
-        BLR_HLOAD(hb[1], (uint32_t)(nk > 1 ? 1 : 0) * N * 4);
+        BLR_HLOAD(hb[1], (uint32_t)(nk > 1 ? 1 : 0) * DRW * 128);
     }
 #pragma unroll
     for (int q = 0; q < P; ++q) BLR_GLOAD(q, q);
@@ -554,14 +571,61 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     BLR_GLOAD(1 % P, P + 1);
     __syncthreads();
     // dh partial row (mt, nt): byte offset of column `lane` of step 0
-    const uint64_t hpbytes = FDH ? (uint64_t)((M + BM - 1) / BM) * ntn * K * 4 : 0;
+    // (rows ordered N tile first, so each path's rows are contiguous)
+    const int64_t mtl = (M + BM - 1) / BM;
+    const uint64_t hpbytes = FDH ? (uint64_t)mtl * ntn * K * 4 : 0;
     const __amdgpu_buffer_rsrc_t rHP = make_rsrc(p.dh_partial, hpbytes);
-    const uint32_t hpoff = (uint32_t)((((int64_t)mt * ntn + nt) * K + (lane & 31)) * 4);
+    const uint32_t hpoff = (uint32_t)((((int64_t)nt * mtl + mt) * K + (lane & 31)) * 4);
     if (!dhw) {
         BLR_AFRAG(fa, 0);
         BLR_BFRAG(fb, bq, 0, 0);
     }
     int b0 = 0, b1 = 1, b2 = 2;  // LDS buffers of steps kt, kt+1 and kt+2
+
+#define BLR_UOFF(i, v, j) ((uint32_t)(((i) * 32 + 8 * ((v) >> 2) + ((v) & 3)) * N + (j) * 32) * 4u)
+    // MP: at the end of path q's ranks the product so far is scaled by the
+    // path's output column scale into yacc (its column partials, if any,
+    // written for path q), and the accumulators restart from zero
+    f32x16_t yacc[MP ? FM : 1][MP ? FN : 1];
+    if (MP) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) yacc[i][j][v] = 0.0f;
+    }
+    // (the epilogue's output addressing, formed here only for MP)
+    const int64_t rl_mp = MP ? m0 + wm * TM + 4 * (lane >> 5) : 0;
+    const int cb_mp = MP ? n0 + wn * TN + (lane & 31) : 0;
+    const uint32_t loff_mp = MP ? (uint32_t)((rl_mp * N + cb_mp) * 4) : 0u;
+    const __amdgpu_buffer_rsrc_t rD_mp = make_rsrc(p.dot_other, (MP && DOT) ? (uint64_t)M * N * 4 : 0);
+#define BLR_FLUSH(q)                                                                       \
+    do {                                                                                   \
+        const float osc_ = -p.oscale;                                                      \
+        const bool full_ = m0 + BM <= M;                                                   \
+        const float *c2p_ = p.out2col + (int64_t)(q) * p.o2_pstride;                       \
+        float c2_[FN], ds_[FN];                                                            \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                   \
+            c2_[j] = c2p_[cb_mp + j * 32];                                                 \
+            ds_[j] = 0.0f;                                                                 \
+        }                                                                                  \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                     \
+            _Pragma("unroll") for (int v = 0; v < 16; ++v)                                 \
+                _Pragma("unroll") for (int j = 0; j < FN; ++j) {                           \
+                    const float val_ = acc[i][j][v] * osc_;                                \
+                    if (DOT) {                                                             \
+                        const bool in_ = full_ || rl_mp + i * 32 + 8 * (v >> 2) + (v & 3) < M; \
+                        ds_[j] += val_ * (in_ ? load_f32_nt(rD_mp, loff_mp, BLR_UOFF(i, v, j)) : 0.0f); \
+                    }                                                                      \
+                    yacc[i][j][v] += val_ * c2_[j];                                        \
+                    acc[i][j][v] = 0.0f;                                                   \
+                }                                                                          \
+        if (DOT) _Pragma("unroll") for (int j = 0; j < FN; ++j) {                          \
+            const float t_ = ds_[j] + __shfl_xor(ds_[j], 32);                              \
+            if (lane < 32) p.dot_partial[(int64_t)(q) * p.dot_pstride + (int64_t)mt * N + cb_mp + j * 32] = t_; \
+        }                                                                                  \
+    } while (0)
 
     // Iteration kt: fragments of step kt+1 are read and decoded while the
     // MFMAs of step kt run, stage kt+2 goes to LDS and stage kt+2+P is
@@ -598,7 +662,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 BLR_DH_MMA(cc[u & 1], hf[u & 1]);
                 BLR_DH_DECODE(hf[(u + 1) & 1], hb[(u + 1) & 1]);
                 const int kn_ = kt + 2 < nk ? kt + 2 : nk - 1;
-                BLR_HLOAD(hb[u & 1], (uint32_t)kn_ * N * 4);
+                BLR_HLOAD(hb[u & 1], (uint32_t)kn_ * DRW * 128);
                 BLR_DH_STORE(rs, kt - 2);
                 BLR_DH_DOT(cc[(u + 1) & 1], d4, kt - 1);
                 BLR_SSTORE((u + 2) % P, (kt + 2) & (NSD - 1));
@@ -655,6 +719,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 b0 = b1;
                 b1 = b2;
                 b2 = b2 == NS - 1 ? 0 : b2 + 1;
+                if (MP && ((kt + 1) * BK) % PKr == 0) BLR_FLUSH((kt + 1) * BK / PKr - 1);
             }
         }
         if (FDH) __syncthreads();  // matches the DH role's final barrier
@@ -673,6 +738,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 #undef BLR_BFRAG
 #undef BLR_MMA
 
+#undef BLR_FLUSH
     // Epilogue from the accumulators: products, tapes, scaled outputs and
     // column partials. Element (i, v, j) of a lane sits at row
     // rl + i*32 + 8*(v/4) + v%4 and column cb + j*32; the lane part of the
@@ -689,11 +755,10 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.dot_other, DOT ? obytes : 0);
     float c2[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) c2[j] = OUT2 ? p.out2col[cb + j * 32] : 0.0f;
+    for (int j = 0; j < FN; ++j) c2[j] = (OUT2 && !MP) ? p.out2col[cb + j * 32] : 0.0f;
     float dsum[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) dsum[j] = 0.0f;
-#define BLR_UOFF(i, v, j) ((uint32_t)(((i) * 32 + 8 * ((v) >> 2) + ((v) & 3)) * N + (j) * 32) * 4u)
 #define BLR_EPI_BLOCK(GUARD)                                                               \
     do {                                                                                   \
         _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                   \
@@ -701,17 +766,17 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
             _Pragma("unroll") for (int v = 0; v < 16; ++v) {                               \
                 const bool in_ = !(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M;     \
                 _Pragma("unroll") for (int j = 0; j < FN; ++j) {                           \
-                    if (DOT) oth[j][v] = in_ ? load_f32_nt(rD, loff, BLR_UOFF(i, v, j)) : 0.0f; \
+                    if (DOT && !MP) oth[j][v] = in_ ? load_f32_nt(rD, loff, BLR_UOFF(i, v, j)) : 0.0f; \
                     if (OUT2) old[j][v] = (p.out2acc && in_) ? load_f32(rO2, loff, BLR_UOFF(i, v, j)) : 0.0f; \
                 }                                                                          \
             }                                                                              \
             _Pragma("unroll") for (int v = 0; v < 16; ++v) {                               \
                 if (!(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M) {                \
                     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                       \
-                        const float val = acc[i][j][v] * osc;                              \
+                        const float val = MP ? yacc[i][j][v] : acc[i][j][v] * osc;         \
                         if (OUT) store_f32(rO, loff, BLR_UOFF(i, v, j), val);              \
-                        if (OUT2) store_f32_nt(rO2, loff, BLR_UOFF(i, v, j), old[j][v] + val * c2[j]); \
-                        if (DOT) dsum[j] += val * oth[j][v];                               \
+                        if (OUT2) store_f32_nt(rO2, loff, BLR_UOFF(i, v, j), old[j][v] + (MP ? val : val * c2[j])); \
+                        if (DOT && !MP) dsum[j] += val * oth[j][v];                        \
                     }                                                                      \
                 }                                                                          \
             }                                                                              \
@@ -726,7 +791,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     }
 #undef BLR_EPI_BLOCK
 #undef BLR_UOFF
-    if (DOT) {
+    if (DOT && !MP) {
         // lanes l and l+32 hold the same columns; then the WM waves of a
         // column strip add in row order
         if (!dhw) {
@@ -747,12 +812,14 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 }
 
 template <int BM, int BN, int WM, int WN, int P, int MINB, bool OUT, bool OUT2, bool DOT, int GM, bool FDH = false,
-          int KB = 2, bool PLANE = false>
+          int KB = 2, bool PLANE = false, bool MP = false>
 static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
     if (a.N % BN != 0 || a.K % 128 != 0 || a.K < 128) return hipErrorInvalidValue;
+    if (a.path_k && (a.path_k % 128 || a.K % a.path_k)) return hipErrorInvalidValue;
+    if (a.path_n && a.path_n % BN) return hipErrorInvalidValue;
     const int64_t tiles = (int64_t)(a.N / BN) * ((a.M + BM - 1) / BM);
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM, FDH, KB, PLANE>),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, P, MINB, OUT, OUT2, DOT, GM, FDH, KB, PLANE, MP>),
                        dim3((unsigned)tiles),
                        dim3((FDH ? 2 : 1) * WM * WN * 64), 0, s, a);
     hipError_t e = hipGetLastError();
@@ -1054,8 +1121,12 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s);
         case GEMM_PLANE: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4, true>(K_GEMM_PLANE, a, s);
+        case GEMM_F2_MP:
+            return launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, false, 8, false, 4, false, true>(K_GEMM_F2, a, s);
+        case GEMM_B2_MP:
+            return launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8, false, 4, false, true>(K_GEMM_B2, a, s);
         case GEMM_B1_DH:
-            switch (a.N) {  // 64 tokens x up to 256 ranks, 64 ranks per wave
+            switch (a.path_n ? a.path_n : a.N) {  // 64 tokens x up to 256 ranks of one path, 64 per wave
                 case 128: return launch_gemm_t<64, 128, 1, 2, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
                 case 256:
                 case 512: return launch_gemm_t<64, 256, 1, 4, 2, 1, true, false, true, 1, true>(K_GEMM_B1_DH, a, s);
@@ -1087,7 +1158,7 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
     int b = (G % NUM_XCD == 0) ? (int)(blockIdx.x % NUM_XCD) * (G / NUM_XCD) + (int)(blockIdx.x / NUM_XCD)
                                : (int)blockIdx.x;
     int j = 0;
-    if (jobs.count > 1 && b >= jobs.job[1].tiles_before) j = 1;
+    while (j + 1 < jobs.count && b >= jobs.job[j + 1].tiles_before) ++j;
     const TnJob &jb = jobs.job[j];
     b -= jb.tiles_before;
     const int ntn = jb.No / TN_BN;
@@ -1105,7 +1176,7 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
     f32x4_t cs;
 #pragma unroll
     for (int e = 0; e < 4; ++e) cs[e] = col[4 * cb + e] * sc;
-    const int64_t ld = bside ? jb.No : jb.Mo;
+    const int64_t ld = bside ? jb.ldb : jb.lda;
     const float *src = (bside ? jb.B + n0 : jb.A + m0) + 4 * cb;
     _Float16 *dst0 = (bside ? &Bs[0][0] : &As[0][0]) + 4 * cb * TN_LDK + 4 * tb;
     constexpr int BUFH = TN_BM * TN_LDK;  // halves per buffer (A and B alike)

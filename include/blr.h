@@ -141,6 +141,35 @@ int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const 
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * A layer of several paths (page: `blr_forward` / `blr_backward` over the
+ * paths of a layer; y is the sum of the paths' outputs), fused: one launch
+ * per contraction for all paths. paths = P, 1 <= P <= 4; path p's operands
+ * are the p-th blocks of
+ *   bits_u [P][d_out][r/32], bits_v [P][d_in][r/32] (16-byte aligned),
+ *   h [P][d_out], l [P][r], g [P][d_in],
+ * and the a tape is [M][P r] (the paths' ranks side by side). There is no c
+ * tape: the backward recomputes each path's c. y (accumulate_y as in
+ * blr_forward) receives sum_p h_p . c_p; dx (accumulate_dx) receives
+ * sum_p g_p . dx'_p; dh [P][d_out], dl [P][r], dg [P][d_in] always
+ * accumulate; with grad_u [P][d_out][r] and grad_v [P][d_in][r] (both or
+ * neither) the sign gradients of every path are formed as in
+ * blr_backward_signs. Sizes: P r obeys the rules for r. The workspace is
+ * blr_workspace_bytes_paths(M, d_in, d_out, r, P) bytes (0 for an invalid
+ * shape). Errors as blr_forward / blr_backward_signs; P out of range is
+ * BLR_ERR_SHAPE. P = 1 gives exactly blr_forward / blr_backward.
+ */
+size_t blr_workspace_bytes_paths(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t paths);
+int blr_forward_paths(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t paths, const float *x,
+                      const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,
+                      float *y, int accumulate_y, float *tape_a, void *workspace, size_t workspace_bytes,
+                      void *stream);
+int blr_backward_paths(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t paths, const float *x,
+                       const float *dy, const uint32_t *bits_u, const uint32_t *bits_v, const float *h,
+                       const float *l, const float *g, const float *tape_a, float gscale, float *dh, float *dl,
+                       float *dg, float *dx, int accumulate_dx, float *grad_u, float *grad_v, int accumulate_signs,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Dense frozen linear (page: `plane_linear`): y [M][n] = (f16(x * scale)
  * . plane^T) / scale, x [M][k] f32, plane [n][k] f16 (IEEE binary16 bit
  * patterns), through the same staging and MFMA contraction as the layer

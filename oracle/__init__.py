@@ -167,6 +167,51 @@ def sign_grads(x, dy, bits_u, bits_v, h, l, g, gu0=None, gv0=None, accumulate: b
     return gu, gv
 
 
+def forward_paths(x, bits_u, bits_v, h, l, g, y0=None, accumulate: bool = False):
+    """A layer of P paths (page: `blr_forward` over a layer's paths: the
+    first path overwrites y unless accumulating, every later path adds):
+    y = sum_p h_p . c_p with path p's operands bits_u[p], bits_v[p], h[p],
+    l[p], g[p]. Returns (y, a) in f64, a [M][P r] (the paths' a side by
+    side)."""
+    h = _f64(h)
+    P = h.shape[0]
+    y, tapes = None if y0 is None else _f64(y0), []
+    for p in range(P):
+        y, a, _ = forward(x, bits_u[p], bits_v[p], h[p], l[p], g[p], y0=y, accumulate=accumulate or p > 0)
+        tapes.append(a)
+    return y, np.concatenate(tapes, axis=1)
+
+
+def backward_paths(x, dy, bits_u, bits_v, h, l, g, dx0=None, accumulate_dx: bool = False):
+    """Backward of a layer of P paths (page: `blr_backward` over the paths,
+    dx overwritten by the first path unless accumulating, added by later
+    ones): dh [P][d_out], dl [P][r], dg [P][d_in] from zero, and
+    dx = sum_p g_p . dx'_p. Returns (dh, dl, dg, dx) in f64."""
+    h = _f64(h)
+    P = h.shape[0]
+    dx, dhs, dls, dgs = None if dx0 is None else _f64(dx0), [], [], []
+    for p in range(P):
+        dh, dl, dg, dx = backward(x, dy, bits_u[p], bits_v[p], h[p], l[p], g[p], dx0=dx,
+                                  accumulate_dx=accumulate_dx or p > 0)
+        dhs.append(dh)
+        dls.append(dl)
+        dgs.append(dg)
+    return np.stack(dhs), np.stack(dls), np.stack(dgs), dx
+
+
+def sign_grads_paths(x, dy, bits_u, bits_v, h, l, g):
+    """The sign gradients of every path of a layer: (G_U [P][d_out][r],
+    G_V [P][d_in][r]) in f64 (each path's, as in sign_grads: y is linear in
+    each path's signs, so the other paths do not enter)."""
+    h = _f64(h)
+    gus, gvs = [], []
+    for p in range(h.shape[0]):
+        gu, gv = sign_grads(x, dy, bits_u[p], bits_v[p], h[p], l[p], g[p])
+        gus.append(gu)
+        gvs.append(gv)
+    return np.stack(gus), np.stack(gvs)
+
+
 def f16_decode(bits) -> np.ndarray:
     """f64 values of IEEE binary16 bit patterns (uint16)."""
     bits = np.ascontiguousarray(bits, dtype=np.uint16)

@@ -157,6 +157,17 @@ def custom(M: int, d_in: int, d_out: int, r: int, seed: int, dy_sigma: float = 1
     return d
 
 
+def custom_paths(M: int, d_in: int, d_out: int, r: int, paths: int, seed: int, dy_sigma: float = 1e-3,
+                 l_hi: float = 0.1) -> dict[str, np.ndarray]:
+    """A layer of `paths` paths: x and dy of path 0's draw, and each path's
+    bitmaps and scales from its own seed (seed + 97 p), stacked along a
+    leading path axis."""
+    per = [custom(M, d_in, d_out, r, seed + 97 * p, dy_sigma=dy_sigma, l_hi=l_hi) for p in range(paths)]
+    d = {k: np.stack([q[k] for q in per]) for k in ("bits_u", "bits_v", "h", "l", "g")}
+    d["x"], d["dy"], d["gscale"] = per[0]["x"], per[0]["dy"], per[0]["gscale"]
+    return d
+
+
 def exact_grid(M: int, d_in: int, d_out: int, r: int, seed: int) -> dict[str, np.ndarray]:
     """Inputs on a grid where every f16-staged forward operand is exact: x in
     (1/8)Z with |x| <= 1/2, g in {0.5, 1}, l in {0.5, 1, 2} (the page's

@@ -229,3 +229,36 @@ def test_plane_linear_rejects_bad_arguments(ptrs):
     assert lib.blr_plane_linear(128, 256, 128, f(), f(), f(), ctypes.c_float(3.0), None) == E_SCALE
     assert lib.blr_plane_linear(128, 256, 128, f(offset=4), f(), f(), ctypes.c_float(1.0), None) == E_ALIGN
     assert len(good) == 8
+
+
+def test_paths_workspace_and_rejects(ptrs):
+    lib = blr.load()
+    one = blr.blr_workspace_bytes(256, 256, 256, 128)
+    assert blr.blr_workspace_bytes_paths(256, 256, 256, 128, 1) == one
+    assert blr.blr_workspace_bytes_paths(256, 256, 256, 128, 3) > one
+    for bad in (0, 5, -1):
+        assert blr.blr_workspace_bytes_paths(256, 256, 256, 128, bad) == 0
+    f = ptrs["_fake"]
+    ws = 1 << 40
+
+    def fwd_p(P, r=128, **kw):
+        q = {k: f() for k in ("x", "bu", "bv", "h", "l", "g", "y", "ta")}
+        q.update(kw)
+        return lib.blr_forward_paths(128, 256, 256, r, P, q["x"], q["bu"], q["bv"], q["h"], q["l"], q["g"], q["y"], 0,
+                                     q["ta"], f(), ws, None)
+
+    assert fwd_p(5) == E_SHAPE
+    assert fwd_p(0) == E_SHAPE
+    assert fwd_p(2, r=96) == E_SHAPE
+    assert fwd_p(2, x=None) == E_NULL
+    assert fwd_p(2, bu=f(offset=4)) == E_ALIGN
+    q = {k: f() for k in KEYS}
+    assert lib.blr_backward_paths(128, 256, 256, 128, 5, q["x"], q["dy"], q["bu"], q["bv"], q["h"], q["l"], q["g"],
+                                  q["ta"], ctypes.c_float(1024.0), q["dh"], q["dl"], q["dg"], q["dx"], 0, None, None,
+                                  0, q["ws"], ws, None) == E_SHAPE
+    assert lib.blr_backward_paths(128, 256, 256, 128, 2, q["x"], q["dy"], q["bu"], q["bv"], q["h"], q["l"], q["g"],
+                                  q["ta"], ctypes.c_float(3.0), q["dh"], q["dl"], q["dg"], q["dx"], 0, None, None,
+                                  0, q["ws"], ws, None) == E_SCALE
+    assert lib.blr_backward_paths(128, 256, 256, 128, 2, q["x"], q["dy"], q["bu"], q["bv"], q["h"], q["l"], q["g"],
+                                  q["ta"], ctypes.c_float(1024.0), q["dh"], q["dl"], q["dg"], q["dx"], 0, f(), None,
+                                  0, q["ws"], ws, None) == E_NULL

@@ -469,3 +469,99 @@ def test_plane_linear_identity_and_dense():
     plane = rng.standard_normal((30, k)).astype(np.float16)
     want = x @ plane.astype(np.float64).T
     assert oracle.rel_frobenius(oracle.plane_linear(x, plane.view(np.uint16)), want) < 1e-14
+
+
+# ------------------------------------------------------------- paths --
+
+def _paths(M, d_in, d_out, r, P, seed):
+    return synth.custom_paths(M, d_in, d_out, r, P, seed, dy_sigma=1.0, l_hi=1.0)
+
+
+def _path(d, p):
+    return {"x": d["x"], "dy": d["dy"], **{k: d[k][p] for k in ("bits_u", "bits_v", "h", "l", "g")}}
+
+
+@pytest.mark.parametrize("M,d_in,d_out,r,P", [(5, 7, 6, 40, 2), (33, 16, 24, 64, 3)])
+def test_paths_forward_matches_dense_sum(M, d_in, d_out, r, P):
+    """y = x . (sum_p W_p)^T with each W_p materialised from numpy's bit
+    unpacking; the tape is the paths' a side by side."""
+    d = _paths(M, d_in, d_out, r, P, 700 + M)
+    y, a = oracle.forward_paths(d["x"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"])
+    W = sum(dense_w(_path(d, p)) for p in range(P))
+    assert oracle.rel_frobenius(y, d["x"].astype(np.float64) @ W.T) < 1e-12
+    assert a.shape == (M, P * r)
+    for p in range(P):
+        SV = unpack_signs(d["bits_v"][p], d_in, r)
+        ap = (d["x"].astype(np.float64) * d["g"][p].astype(np.float64)) @ SV
+        assert oracle.rel_frobenius(a[:, p * r:(p + 1) * r], ap) < 1e-12
+
+
+def test_paths_backward_central_differences_and_dense():
+    """Each path's dh, dl, dg are exact central differences of
+    L = sum(dy . y) of the whole layer (y is linear in every parameter);
+    dx = dy . sum_p W_p."""
+    M, d_in, d_out, r, P = 3, 5, 4, 33, 2
+    d = _paths(M, d_in, d_out, r, P, 711)
+    dh, dl, dg, dx = oracle.backward_paths(d["x"], d["dy"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"])
+    W = sum(dense_w(_path(d, p)) for p in range(P))
+    assert oracle.rel_frobenius(dx, d["dy"].astype(np.float64) @ W) < 1e-12
+
+    def L(**kw):
+        q = {k: d[k].astype(np.float64).copy() for k in ("h", "l", "g")}
+        q.update(kw)
+        y, _ = oracle.forward_paths(d["x"], d["bits_u"], d["bits_v"], q["h"], q["l"], q["g"])
+        return float(np.sum(d["dy"].astype(np.float64) * y))
+
+    eps = 0.25
+    for name, got in (("h", dh), ("l", dl), ("g", dg)):
+        base = d[name].astype(np.float64)
+        fd = np.empty(base.shape)
+        for idx in np.ndindex(base.shape):
+            plus, minus = base.copy(), base.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            fd[idx] = (L(**{name: plus}) - L(**{name: minus})) / (2 * eps)
+        assert oracle.rel_frobenius(got, fd) < 1e-10, name
+
+
+def test_paths_identical_paths_and_permutation():
+    """Two copies of one path double y and dx and repeat its own dh, dl, dg;
+    reordering the paths reorders the per-path gradients and leaves y, dx."""
+    M, d_in, d_out, r = 9, 12, 10, 40
+    one = _paths(M, d_in, d_out, r, 1, 720)
+    two = {k: (np.concatenate([v, v]) if k in ("bits_u", "bits_v", "h", "l", "g") else v) for k, v in one.items()}
+    y1, _ = oracle.forward_paths(one["x"], one["bits_u"], one["bits_v"], one["h"], one["l"], one["g"])
+    y2, _ = oracle.forward_paths(two["x"], two["bits_u"], two["bits_v"], two["h"], two["l"], two["g"])
+    assert np.allclose(y2, 2 * y1, rtol=0, atol=1e-12 * np.abs(y1).max())
+    g1 = oracle.backward_paths(one["x"], one["dy"], one["bits_u"], one["bits_v"], one["h"], one["l"], one["g"])
+    g2 = oracle.backward_paths(two["x"], two["dy"], two["bits_u"], two["bits_v"], two["h"], two["l"], two["g"])
+    for a, b in zip(g1[:3], g2[:3]):
+        assert np.array_equal(b[0], a[0]) and np.array_equal(b[1], a[0])
+    assert np.allclose(g2[3], 2 * g1[3], rtol=0, atol=1e-12 * np.abs(g1[3]).max())
+    d = _paths(M, d_in, d_out, r, 3, 730)
+    perm = [2, 0, 1]
+    q = {k: (d[k][perm] if k in ("bits_u", "bits_v", "h", "l", "g") else d[k]) for k in d}
+    ya, _ = oracle.forward_paths(d["x"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"])
+    yb, _ = oracle.forward_paths(q["x"], q["bits_u"], q["bits_v"], q["h"], q["l"], q["g"])
+    assert oracle.rel_frobenius(yb, ya) < 1e-13
+    ga = oracle.backward_paths(d["x"], d["dy"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"])
+    gb = oracle.backward_paths(q["x"], q["dy"], q["bits_u"], q["bits_v"], q["h"], q["l"], q["g"])
+    for a, b in zip(ga[:3], gb[:3]):
+        assert np.array_equal(b, a[perm])
+    assert oracle.rel_frobenius(gb[3], ga[3]) < 1e-13
+
+
+def test_paths_sign_grads_are_each_paths_own():
+    """A path's sign gradients do not depend on the other paths (y is a sum
+    over paths); they pass the relaxed flip identity of a single path."""
+    M, d_in, d_out, r, P = 6, 9, 7, 40, 2
+    d = _paths(M, d_in, d_out, r, P, 740)
+    gu, gv = oracle.sign_grads_paths(d["x"], d["dy"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"])
+    for p in range(P):
+        su, sv = oracle.sign_grads(d["x"], d["dy"], d["bits_u"][p], d["bits_v"][p], d["h"][p], d["l"][p], d["g"][p])
+        assert np.array_equal(gu[p], su) and np.array_equal(gv[p], sv)
+    # Euler: sum_k S_U . G_U = h . dh per path, against the paths' backward
+    dh, _, dg, _ = oracle.backward_paths(d["x"], d["dy"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"])
+    for p in range(P):
+        SU = unpack_signs(d["bits_u"][p], d_out, r)
+        assert oracle.rel_frobenius((SU * gu[p]).sum(1), d["h"][p] * dh[p]) < 1e-12
