@@ -267,6 +267,36 @@ def main():
                 "frac_f16_peak": round(sf / (s_us * 1e-6) / 1e12 / PEAK_F16_TFLOPS, 4),
                 "gbs": round(sb / (s_us * 1e-6) / 1e9, 1)}
 
+    # the fused layer of two paths of half the rank each (same MFMA work as
+    # the one-path step): blr_forward_paths + blr_backward_paths
+    multi = None
+    if r % 256 == 0:
+        P, rp = 2, r // 2
+        dp = synth.custom_paths(M, di, do, rp, P, seed=9100, dy_sigma=w.dy_sigma, l_hi=w.l_hi)
+        tp = {k: torch.from_numpy(np.ascontiguousarray(dp[k].view(np.int32) if dp[k].dtype == np.uint32 else dp[k]))
+              .to(dev) for k in ("bits_u", "bits_v", "h", "l", "g")}
+        yp = torch.empty((M, do), dtype=torch.float32, device=dev)
+        tap = torch.empty((M, P * rp), dtype=torch.float32, device=dev)
+        dhp = torch.zeros((P, do), dtype=torch.float32, device=dev)
+        dlp = torch.zeros((P, rp), dtype=torch.float32, device=dev)
+        dgp = torch.zeros((P, di), dtype=torch.float32, device=dev)
+        wsp = blr.workspace_paths(M, di, do, rp, P, dev)
+
+        def step_p():
+            blr.blr_forward_paths(t["x"], tp["bits_u"], tp["bits_v"], tp["h"], tp["l"], tp["g"], y=yp, tape_a=tap,
+                                  ws=wsp)
+            blr.blr_backward_paths(t["x"], t["dy"], tp["bits_u"], tp["bits_v"], tp["h"], tp["l"], tp["g"], tap,
+                                   w.gscale, dh=dhp, dl=dlp, dg=dgp, dx=dx, ws=wsp)
+
+        for _ in range(max(args.warmup, 1)):
+            step_p()
+        torch.cuda.synchronize()
+        ms_p = timed(step_p, args.steps)
+        fl = 6.0 * M * P * rp * (di + do)
+        multi = {"paths": P, "rank_per_path": rp, "ms_per_step": round(ms_p, 5),
+                 "tokens_per_s": round(M / (ms_p / 1000.0), 1), "tflops_metric": round(fl / (ms_p / 1000.0) / 1e12, 2)}
+        del tp, yp, tap, dhp, dlp, dgp, wsp
+
     tokens_s = M / (ms / 1000.0)
     tf_metric = w.flops_metric() / (ms / 1000.0) / 1e12
     tf_mfma = w.flops_mfma() / (ms / 1000.0) / 1e12
@@ -294,6 +324,7 @@ def main():
         "kernels": kernels,
         "roofline": roof,
         "sign_grads": sign,
+        "multi_path": multi,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
