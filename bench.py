@@ -58,8 +58,9 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
     if name == "transpose_bits":     # one bitmap in, its transpose out (average of U and V)
         return 2 * r * (di + do) / 2 / 8, 0.0
     if name == "colsum_finish":      # read the column partials of dh, dl, dg
-        rows_hl = 32 if (not keep_c and r in (128, 256, 512)) else 64  # the fused B1 launch covers 32 tokens
-        return (-(-M // rows_hl) * (do + r) + -(-M // 64) * di) * f32, 0.0
+        mt = -(-M // 64)  # every producer uses 64-token tiles; fused dh at r = 512: two rank tiles
+        rows_h = 2 * mt if (not keep_c and r == 512) else mt
+        return (rows_h * do + mt * (r + di)) * f32, 0.0
     if name == "expand_signs":       # per launch: one bitmap in, one f16 plane out (average of U and V)
         rows = (di + do) / 2
         return rows * (r / 8 + r * 2), 0.0
