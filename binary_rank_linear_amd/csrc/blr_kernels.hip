@@ -759,7 +759,12 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     float dsum[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) dsum[j] = 0.0f;
-#define BLR_EPI_BLOCK(GUARD)                                                               \
+    // (GUARD: check rows against M; ACC: y or dx accumulate, so the old
+    // values are loaded. The common case, a full tile written without
+    // accumulation, has its own copy with no load: a load under a
+    // per-element condition makes every store after it wait for all earlier
+    // stores, which share the load counter.)
+#define BLR_EPI_BLOCK(GUARD, ACC)                                                          \
     do {                                                                                   \
         _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                   \
             float oth[DOT ? FN : 1][DOT ? 16 : 1], old[OUT2 ? FN : 1][OUT2 ? 16 : 1];      \
@@ -767,7 +772,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 const bool in_ = !(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M;     \
                 _Pragma("unroll") for (int j = 0; j < FN; ++j) {                           \
                     if (DOT && !MP) oth[j][v] = in_ ? load_f32_nt(rD, loff, BLR_UOFF(i, v, j)) : 0.0f; \
-                    if (OUT2) old[j][v] = (p.out2acc && in_) ? load_f32(rO2, loff, BLR_UOFF(i, v, j)) : 0.0f; \
+                    if (OUT2) old[j][v] = ((ACC) && in_) ? load_f32(rO2, loff, BLR_UOFF(i, v, j)) : 0.0f; \
                 }                                                                          \
             }                                                                              \
             _Pragma("unroll") for (int v = 0; v < 16; ++v) {                               \
@@ -783,10 +788,10 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         }                                                                                  \
     } while (0)
     if (!dhw) {
-        if (full) {
-            BLR_EPI_BLOCK(false);
+        if (full && !(OUT2 && p.out2acc)) {
+            BLR_EPI_BLOCK(false, false);
         } else {
-            BLR_EPI_BLOCK(true);
+            BLR_EPI_BLOCK(true, p.out2acc);
         }
     }
 #undef BLR_EPI_BLOCK
@@ -1006,7 +1011,7 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
         float dsum[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) dsum[j] = 0.0f;
-#define AS_EPI(GUARD)                                                                      \
+#define AS_EPI(GUARD, ACC) /* as BLR_EPI_BLOCK */                                           \
         do {                                                                               \
             _Pragma("unroll") for (int i = 0; i < FM; ++i) {                               \
                 /* one row block at a time: 16 uniform row offsets live */                  \
@@ -1017,7 +1022,7 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
                 _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
                     const bool in_ = !(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M; \
                     _Pragma("unroll") for (int j = 0; j < FN; ++j)                         \
-                        if (OUT2) old[j][v] = (p.out2acc && in_) ? load_f32(rO2, lo_, AS_UOFF(i, v, j)) : 0.0f; \
+                        if (OUT2) old[j][v] = ((ACC) && in_) ? load_f32(rO2, lo_, AS_UOFF(i, v, j)) : 0.0f; \
                 }                                                                          \
                 _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
                     if (!(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M) {            \
@@ -1031,10 +1036,10 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
                 }                                                                          \
             }                                                                              \
         } while (0)
-        if (full) {
-            AS_EPI(false);
+        if (full && !(OUT2 && p.out2acc)) {
+            AS_EPI(false, false);
         } else {
-            AS_EPI(true);
+            AS_EPI(true, p.out2acc);
         }
 #undef AS_EPI
 #undef AS_UOFF
