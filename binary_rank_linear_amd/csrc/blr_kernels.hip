@@ -895,6 +895,25 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
         constexpr int UNR = nch / 256 < 32 ? nch / 256 : 32;
         constexpr bool onecol = 256 % cpr == 0;
         const f32x4_t c1 = onecol ? load_f32x4(rC, (uint32_t)(16 * (tid % cpr)), 0u) : f32x4_t{};
+        if (onecol && m0 + AS_BM <= M) {
+            // full block: thread tid takes rows tid / cpr + u * (256 / cpr) of
+            // column group tid % cpr; the row step is a uniform offset, so
+            // every load is issued before the first is waited for
+            constexpr int rstep = 256 / (onecol ? cpr : 256);
+            const int r0 = tid / cpr, c4 = tid % cpr;
+            const uint32_t vb = (uint32_t)(((m0 + r0) * p.lda + 4 * c4) * 4);
+            f32x4_t v[nch / 256];
+#pragma unroll
+            for (int u = 0; u < nch / 256; ++u) v[u] = load_f32x4(rA, vb, (uint32_t)(u * rstep * p.lda * 4));
+            const f32x4_t cs = c1 * p.ascale;
+#pragma unroll
+            for (int u = 0; u < nch / 256; ++u) {
+                uint2 h;
+                h.x = f16x2_scaled(v[u].x, cs.x, v[u].y, cs.y);
+                h.y = f16x2_scaled(v[u].z, cs.z, v[u].w, cs.w);
+                *reinterpret_cast<uint2 *>(As + (r0 + u * rstep) * LDK + 4 * c4) = h;
+            }
+        } else
         for (int i0 = 0; i0 < nch; i0 += 256 * UNR) {
             f32x4_t v[UNR], c[onecol ? 1 : UNR];
 #pragma unroll
