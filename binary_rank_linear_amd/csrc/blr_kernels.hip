@@ -278,9 +278,10 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // partials need every row of a column in one wave
     static_assert(!MP || (WM == 1 && !OUT && !FDH && !PLANE), "paths along K");
     // Fused dh (B1 only): 64-token tiles, one row of waves with 64 ranks
-    // each, and as many more waves in a second role (DH waves): they
-    // stage the f32 dy tile and compute the dh partials, so each SIMD holds
-    // one wave of each role and one's VALU work overlaps the other's MFMAs.
+    // each, and as many more waves in a second role (DH waves) that compute
+    // the dh partials from an f32 copy of the dy tile the B1 waves also
+    // stage, so each SIMD holds one wave of each role and one's VALU work
+    // overlaps the other's MFMAs.
     static_assert(!FDH || (WM == 1 && BM == 64 && TN == 64 && DOT && OUT), "fused dh shape");
     constexpr int FMD = BM / 32;    // fused dh: row blocks of the recomputed c
     constexpr int KD = TN / 16;     // fused dh: MFMA k-blocks over the wave's ranks (FMD * KD = 8)
@@ -418,9 +419,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 #define BLR_GLOAD(q, kt)                                                                   \
     do {                                                                                   \
         const int k_ = (kt) < nk ? (kt) : nk - 1;                                          \
-        _Pragma("unroll") for (int v = 0; v < PER; ++v) ar[q][v] =                         \
-            load_f32x4(rA, aoff[v], (uint32_t)k_ * (BK * 4));                              \
-        if (!PLANE && !dhw) cr[q] = load_f32x4(rC, coff, (uint32_t)k_ * (BK * 4));         \
+        if (!dhw) {                                                                        \
+            _Pragma("unroll") for (int v = 0; v < PER; ++v) ar[q][v] =                     \
+                load_f32x4(rA, aoff[v], (uint32_t)k_ * (BK * 4));                          \
+            if (!PLANE) cr[q] = load_f32x4(rC, coff, (uint32_t)k_ * (BK * 4));             \
+        }                                                                                  \
     } while (0)
 
 #define BLR_BLOAD(dst, grp4)                                                               \
@@ -433,18 +436,19 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
             load_u32x4(rB, boff[j], so_);                                                  \
     } while (0)
 
-#define BLR_SSTORE(q, buf)                                                                 \
+#define BLR_SSTORE(q, buf, dbuf)                                                           \
     do {                                                                                   \
-        if (dhw) {                                                                         \
-            /* DH role: the f32 dy tile, transposed (rows past M hold row                  \
-               M-1, a finite copy: the recomputed c is zero there); row bit 3 is           \
-               flipped in columns 16-31, which spreads a write's 64 lanes                  \
-               over distinct banks */                                                      \
-            _Pragma("unroll") for (int v = 0; v < PER; ++v) {                              \
-                float *dt_ = dyT + (buf) * (32 * LDR) + ((arow + v * RPP) ^ (8 * (c4 >> 2))); \
-                _Pragma("unroll") for (int e = 0; e < 4; ++e) dt_[(4 * c4 + e) * LDR] = ar[q][v][e]; \
+        if (!dhw) {                                                                        \
+            if (FDH) {                                                                     \
+                /* for the DH role: the f32 dy tile, transposed, in dy ring slot           \
+                   dbuf (rows past M hold row M-1, a finite copy: the recomputed           \
+                   c is zero there); row bit 3 is flipped in columns 16-31, which          \
+                   spreads a write's 64 lanes over distinct banks */                       \
+                _Pragma("unroll") for (int v = 0; v < PER; ++v) {                          \
+                    float *dt_ = dyT + (dbuf) * (32 * LDR) + ((arow + v * RPP) ^ (8 * (c4 >> 2))); \
+                    _Pragma("unroll") for (int e = 0; e < 4; ++e) dt_[(4 * c4 + e) * LDR] = ar[q][v][e]; \
+                }                                                                          \
             }                                                                              \
-        } else {                                                                           \
             const f32x4_t cs_ = PLANE ? f32x4_t{p.ascale, p.ascale, p.ascale, p.ascale}    \
                                       : cr[q] * p.ascale;                                  \
             _Float16 *dst_ = As + (buf) * (BM * LDK) + wofs;                               \
@@ -565,9 +569,9 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         BLR_BLOAD(bq, 0);
         BLR_BLOAD(bn, 1);
     }
-    BLR_SSTORE(0, 0);
+    BLR_SSTORE(0, 0, 0);
     BLR_GLOAD(0, P);
-    BLR_SSTORE(1 % P, 1);
+    BLR_SSTORE(1 % P, 1, 1);
     BLR_GLOAD(1 % P, P + 1);
     __syncthreads();
     // dh partial row (mt, nt): byte offset of column `lane` of step 0
@@ -638,7 +642,8 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         // sums. Iteration kt: MFMAs of step kt, signs of step kt+1 (words
         // loaded an iteration ago), words of step kt+2, the dot of step kt-1
         // (its dy in ring slot (kt-1) % 4, rewritten only after this
-        // iteration's barrier), the dh store of step kt-2, and stage kt+2.
+        // iteration's barrier) and the dh store of step kt-2; the B1 waves
+        // stage dy.
         // The iteration is one basic block: the dot of step -1 (iteration 0)
         // multiplies a zero c by whatever slot 3 holds, and its sums and the
         // stores of steps -2 and -1 are never kept.
@@ -665,8 +670,6 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 BLR_HLOAD(hb[u & 1], (uint32_t)kn_ * DRW * 128);
                 BLR_DH_STORE(rs, kt - 2);
                 BLR_DH_DOT(cc[(u + 1) & 1], d4, kt - 1);
-                BLR_SSTORE((u + 2) % P, (kt + 2) & (NSD - 1));
-                BLR_GLOAD((u + 2) % P, kt + 2 + P);
                 // the dy reads first, then each MFMA followed by VALU work
                 // (decode, dot, sums), which issues while the MFMA runs
                 __builtin_amdgcn_sched_group_barrier(0x100, 4 * FMD + WN, 0);
@@ -710,7 +713,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                     for (int j = 0; j < FN; ++j) bq[j] = bn[j];
                     BLR_BLOAD(bn, kt0 / U + 2);
                 }
-                BLR_SSTORE((u + 2) % P, b2);
+                BLR_SSTORE((u + 2) % P, b2, (kt + 2) & (NSD - 1));
                 BLR_GLOAD((u + 2) % P, kt + 2 + P);
                 __syncthreads();
                 // keep later steps' work out of this one: hoisted above the
