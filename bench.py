@@ -51,6 +51,10 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
         return M * (do + 2 * r) * f32 + 2 * r * do / 8 + do * f32 + r * f32, 4.0 * M * r * do
     if name == "gemm_b2_dbl_svt":    # read db and x, write dx
         return M * (r + 2 * di) * f32 + di * r / 8 + (r + di) * f32, 2.0 * M * di * r
+    if name == "gemm_f2_two_paths":  # the two-path layer's F2 (the paths' ranks add up to r)
+        return kernel_work("gemm_f2_al_sut", w)
+    if name == "gemm_b2_two_paths":  # the two-path layer's B2
+        return kernel_work("gemm_b2_dbl_svt", w)
     if name == "gemm_sign_grads":    # read dy, a, x, db; write G_U, G_V
         return M * (do + di + 2 * r) * f32 + (do + di) * r * f32, 2.0 * M * r * (do + di)
     if name == "colsum_dy_c":        # read dy and c
