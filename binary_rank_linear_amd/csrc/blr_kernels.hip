@@ -282,11 +282,16 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     // the dh partials from an f32 copy of the dy tile the B1 waves also
     // stage, so each SIMD holds one wave of each role and one's VALU work
     // overlaps the other's MFMAs.
-    static_assert(!FDH || (WM == 1 && BM == 64 && TN == 64 && DOT && OUT), "fused dh shape");
+    static_assert(!FDH || (WM == 1 && BM == 64 && TN == 64 && BK == 32 && DOT && OUT), "fused dh shape");
     constexpr int FMD = BM / 32;    // fused dh: row blocks of the recomputed c
     constexpr int KD = TN / 16;     // fused dh: MFMA k-blocks over the wave's ranks (FMD * KD = 8)
     constexpr int CP = 2 / FMD;     // fused dh: accumulators per row block (two MFMA chains in flight)
-    constexpr int LDR = BM + 4;     // floats per column of the transposed f32 dy tile (pad)
+    // fused dh: floats per column of the transposed f32 dy tile; element
+    // (column c, row m) sits at c * LDR + (m ^ 4 * ((c >> 2) & 7)). With this
+    // pitch and swizzle neither the stagers' 4-byte writes (a float4 of a row
+    // per lane) nor the DH waves' 16-byte reads (4 rows of a column per lane)
+    // meet a bank conflict on gfx950 (measured)
+    constexpr int LDR = BM + 16;
 
     __shared__ __attribute__((aligned(16))) _Float16 As[NS * BM * LDK];
     __shared__ float red[DOT ? WM * BN : 1];
@@ -442,10 +447,10 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
             if (FDH) {                                                                     \
                 /* for the DH role: the f32 dy tile, transposed, in dy ring slot           \
                    dbuf (rows past M hold row M-1, a finite copy: the recomputed           \
-                   c is zero there); row bit 3 is flipped in columns 16-31, which          \
-                   spreads a write's 64 lanes over distinct banks */                       \
+                   c is zero there); the lane's columns 4 c4..4 c4+3 share the row         \
+                   swizzle 4 c4 */                                                         \
                 _Pragma("unroll") for (int v = 0; v < PER; ++v) {                          \
-                    float *dt_ = dyT + (dbuf) * (32 * LDR) + ((arow + v * RPP) ^ (8 * (c4 >> 2))); \
+                    float *dt_ = dyT + (dbuf) * (32 * LDR) + ((arow + v * RPP) ^ (4 * c4)); \
                     _Pragma("unroll") for (int e = 0; e < 4; ++e) dt_[(4 * c4 + e) * LDR] = ar[q][v][e]; \
                 }                                                                          \
             }                                                                              \
@@ -513,7 +518,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         _Pragma("unroll") for (int i = 0; i < FMD; ++i)                                    \
             _Pragma("unroll") for (int q = 0; q < 4; ++q) D4[i][q] =                       \
                 *reinterpret_cast<const f32x4_t *>(dyT + (BUF) * (32 * LDR) + (lane & 31) * LDR + \
-                                                   32 * i + 4 * (lane >> 5) + 8 * (q ^ ((lane >> 4) & 1))); \
+                                                   32 * i + ((4 * (lane >> 5) + 8 * q) ^ (4 * ((lane >> 2) & 7)))); \
     } while (0)
 #define BLR_DH_DOT(CC, D4, KT)                                                             \
     do {                                                                                   \
