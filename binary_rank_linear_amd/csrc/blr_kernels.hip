@@ -268,7 +268,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     constexpr int RPP = NT / TPR;   // activation rows per pass
     constexpr int PER = BM / RPP;   // float4 per thread per stage
     static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % RPP == 0 && PER >= 1, "tile shape");
-    static_assert((KB == 2 || KB == 4) && U % P == 0, "the register ring must divide the unroll");
+    static_assert((KB == 2 || KB == 4) && (2 * U) % P == 0, "the register ring must divide the unroll");
     static_assert(!FDH || KB == 2, "fused dh walks 32-column steps");
     // PLANE (dense frozen linear): the B fragments are read from an f16
     // plane [N][K] (one 16-byte load per lane and k-block, one step ahead)
@@ -696,30 +696,49 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         BLR_DH_SUMLOAD(rs, nk - 1);
         BLR_DH_STORE(rs, nk - 1);
     } else {
-        for (int kt0 = 0; kt0 < nk; kt0 += U) {
+        // Two bitmap groups per iteration: group g's words in bq, group g+1's
+        // in bn; each buffer is refilled (group g+2, g+3) right after its
+        // last step's decode, so no register copy carries words across the
+        // back edge. An odd last group leaves after the first half.
+        for (int kt0 = 0; kt0 < nk; kt0 += 2 * U) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int kt = kt0 + u;
-                if (u % 2 == 0) {
+            for (int u2 = 0; u2 < 2 * U; ++u2) {
+                if (u2 == U && kt0 + U >= nk) break;
+                const int u = u2 % U;        // step within its group
+                const bool second = u2 >= U; // the group of this step is in bn
+                const int kt = kt0 + u2;
+                if (u2 % 2 == 0) {
                     BLR_AFRAG(fa2, b1);
-                    BLR_BFRAG(fb2, bq, u + 1, kt + 1);
+                    if (second) {
+                        BLR_BFRAG(fb2, bn, u + 1, kt + 1);
+                    } else {
+                        BLR_BFRAG(fb2, bq, u + 1, kt + 1);
+                    }
                     BLR_MMA(fa, fb);
                 } else {
                     BLR_AFRAG(fa, b1);
                     if (u < U - 1) {
-                        BLR_BFRAG(fb, bq, u + 1, kt + 1);
+                        if (second) {
+                            BLR_BFRAG(fb, bn, u + 1, kt + 1);
+                        } else {
+                            BLR_BFRAG(fb, bq, u + 1, kt + 1);
+                        }
+                    } else if (second) {
+                        BLR_BFRAG(fb, bq, 0, kt + 1);
                     } else {
                         BLR_BFRAG(fb, bn, 0, kt + 1);
                     }
                     BLR_MMA(fa2, fb2);
                 }
                 if (u == U - 1) {
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) bq[j] = bn[j];
-                    BLR_BLOAD(bn, kt0 / U + 2);
+                    if (second) {
+                        BLR_BLOAD(bn, kt0 / U + 3);
+                    } else {
+                        BLR_BLOAD(bq, kt0 / U + 2);
+                    }
                 }
-                BLR_SSTORE((u + 2) % P, b2, (kt + 2) & (NSD - 1));
-                BLR_GLOAD((u + 2) % P, kt + 2 + P);
+                BLR_SSTORE((u2 + 2) % P, b2, (kt + 2) & (NSD - 1));
+                BLR_GLOAD((u2 + 2) % P, kt + 2 + P);
                 __syncthreads();
                 // keep later steps' work out of this one: hoisted above the
                 // barrier it would wait for loads issued just before
@@ -1135,7 +1154,13 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     const bool wide = a.N % 256 == 0;
     const bool as = wide && a.K <= AS_KMAX;  // activation block held in LDS
     switch (kind) {
-        case GEMM_F1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
+        case GEMM_F1:
+            // 256 columns per tile when they stay inside one path: the x tile
+            // is staged once for twice the columns, and with one workgroup per
+            // CU four stages of x are loaded ahead
+            if ((a.path_n ? a.path_n : a.N) % 256 == 0)
+                return launch_gemm_t<64, 256, 1, 4, 4, 1, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
+            return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
         case GEMM_F2:
             if (as) return launch_gemm_as<true, true, false>(K_GEMM_F2, a, s);
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, true, true, false, 8, false, 4>(K_GEMM_F2, a, s)
