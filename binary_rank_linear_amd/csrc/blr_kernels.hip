@@ -152,6 +152,11 @@ constexpr int NUM_XCD = 8;
 // kept, overflow gives inf). On gfx950 this is two multiplies and one
 // packed conversion, all of which issue while an MFMA runs (a fused
 // multiply-and-convert to f16 does not).
+// v from the lane that DPP control CTRL selects (quad_perm / row_shl)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ uint32_t f16x2_scaled(float a0, float s0, float a1, float s1) {
     typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     half2_t h;
@@ -532,28 +537,24 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 }                                                                          \
         redh[((KT) & 1) * (WN * 64) + wn * 64 + lane] = (dq_[0] + dq_[1]) + (dq_[2] + dq_[3]); \
     } while (0)
-    // the first DH wave adds the waves' dh sums of step KT (after that
-    // step's barrier);
-    // the fragments hold -S, hence the sign
-    // Straight-line (no branch splits the DH iteration): every DH lane adds
-    // the sums of its column (two lanes per wave hold rows of one column),
-    // and only lanes 0-31 of the first DH wave, for a step >= 0, store; the
-    // others' byte offset lies past the partials' buffer range, and the
-    // buffer unit drops an out-of-range store.
-#define BLR_DH_SUMLOAD(RS, KT)                                                             \
+    // The dh sums of step KT (after that step's barrier), formed by the B1
+    // waves, which would otherwise wait at the barrier: a column's 2 WN
+    // partials (WN DH waves, two lane halves each) sit in 2 WN consecutive
+    // lanes of one B1 wave (32 / WN columns a wave), which fold them with
+    // DPP adds (pairs, then quads, then octets) and store from the first
+    // lane; the fragments hold -S, hence the sign. The others' byte offset
+    // lies past the partials' buffer range, and the buffer unit drops an
+    // out-of-range store.
+#define BLR_B1_DHSUM(KT)                                                                   \
     do {                                                                                   \
-        const float *rr_ = redh + ((KT) & 1) * (WN * 64) + (lane & 31);                    \
-        _Pragma("unroll") for (int w = 0; w < WN; ++w) {                                   \
-            RS[2 * w] = rr_[w * 64];                                                       \
-            RS[2 * w + 1] = rr_[w * 64 + 32];                                              \
-        }                                                                                  \
-    } while (0)
-#define BLR_DH_STORE(RS, KT)                                                               \
-    do {                                                                                   \
-        float s_ = 0.0f;                                                                   \
-        _Pragma("unroll") for (int w = 0; w < WN; ++w) s_ += RS[2 * w] + RS[2 * w + 1];    \
-        const bool st_ = rwave == 0 && lane < 32 && (KT) >= 0;                             \
-        store_f32(rHP, st_ ? hpoff + (uint32_t)(KT) * 128u : 0xFFFFFF00u, 0u, -s_);        \
+        constexpr int PW_ = 2 * WN;  /* partials per column */                            \
+        const int pi_ = lane % PW_;                                                        \
+        float v_ = redh[((KT) & 1) * (WN * 64) + (pi_ >> 1) * 64 + (32 / WN) * rwave + lane / PW_ + 32 * (pi_ & 1)]; \
+        v_ += dpp_f32<0xB1>(v_);                    /* lane ^ 1 */                         \
+        v_ += dpp_f32<0x4E>(v_);                    /* lane ^ 2 */                         \
+        if (PW_ == 8) v_ += dpp_f32<0x104>(v_);     /* lane + 4 (row_shl:4) */             \
+        const bool st_ = pi_ == 0 && (KT) >= 0;                                            \
+        store_f32(rHP, st_ ? hpoff + (uint32_t)(KT) * 128u : 0xFFFFFF00u, 0u, -v_);        \
     } while (0)
 
     // Prologue: stages 0 and 1 into LDS buffers 0 and 1, the register ring
@@ -584,7 +585,9 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     const int64_t mtl = (M + BM - 1) / BM;
     const uint64_t hpbytes = FDH ? (uint64_t)mtl * ntn * K * 4 : 0;
     const __amdgpu_buffer_rsrc_t rHP = make_rsrc(p.dh_partial, hpbytes);
-    const uint32_t hpoff = (uint32_t)((((int64_t)nt * mtl + mt) * K + (lane & 31)) * 4);
+    // (the B1 wave's column: 32 / WN columns a wave, 2 WN lanes a column)
+    const uint32_t hpoff =
+        (uint32_t)((((int64_t)nt * mtl + mt) * K + (32 / WN) * rwave + lane / (2 * WN)) * 4);
     if (!dhw) {
         BLR_AFRAG(fa, 0);
         BLR_BFRAG(fb, bq, 0, 0);
@@ -666,18 +669,15 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int kt = kt0 + u;
-                float rs[2 * WN];  // the dh sums of step kt-2
                 BLR_DH_DYLOAD(d4, (kt + NSD - 1) & (NSD - 1));
-                BLR_DH_SUMLOAD(rs, kt - 2);
                 BLR_DH_MMA(cc[u & 1], hf[u & 1]);
                 BLR_DH_DECODE(hf[(u + 1) & 1], hb[(u + 1) & 1]);
                 const int kn_ = kt + 2 < nk ? kt + 2 : nk - 1;
                 BLR_HLOAD(hb[u & 1], (uint32_t)kn_ * DRW * 128);
-                BLR_DH_STORE(rs, kt - 2);
                 BLR_DH_DOT(cc[(u + 1) & 1], d4, kt - 1);
                 // the dy reads first, then each MFMA followed by VALU work
-                // (decode, dot, sums), which issues while the MFMA runs
-                __builtin_amdgcn_sched_group_barrier(0x100, 4 * FMD + WN, 0);
+                // (decode, dot), which issues while the MFMA runs
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 * FMD, 0);
 #pragma unroll
                 for (int m_ = 0; m_ < 8; ++m_) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -687,14 +687,9 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        float rs[2 * WN];
         BLR_DH_DYLOAD(d4, (nk - 1) & (NSD - 1));
-        BLR_DH_SUMLOAD(rs, nk - 2);
-        BLR_DH_STORE(rs, nk - 2);
         BLR_DH_DOT(cc[1], d4, nk - 1);  // nk is a multiple of 4: step nk-1 is odd
         __syncthreads();
-        BLR_DH_SUMLOAD(rs, nk - 1);
-        BLR_DH_STORE(rs, nk - 1);
     } else {
         // Two bitmap groups per iteration: group g's words in bq, group g+1's
         // in bn; each buffer is refilled (group g+2, g+3) right after its
@@ -737,6 +732,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                         BLR_BLOAD(bq, kt0 / U + 2);
                     }
                 }
+                if (FDH) BLR_B1_DHSUM(kt - 2);
                 BLR_SSTORE((u2 + 2) % P, b2, (kt + 2) & (NSD - 1));
                 BLR_GLOAD((u2 + 2) % P, kt + 2 + P);
                 __syncthreads();
@@ -749,14 +745,17 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 if (MP && ((kt + 1) * BK) % PKr == 0) BLR_FLUSH((kt + 1) * BK / PKr - 1);
             }
         }
-        if (FDH) __syncthreads();  // matches the DH role's final barrier
+        if (FDH) {
+            BLR_B1_DHSUM(nk - 2);
+            __syncthreads();  // matches the DH role's final barrier
+            BLR_B1_DHSUM(nk - 1);
+        }
     }
 #undef BLR_DH_DYLOAD
 #undef BLR_DH_DECODE
 #undef BLR_DH_MMA
 #undef BLR_DH_DOT
-#undef BLR_DH_SUMLOAD
-#undef BLR_DH_STORE
+#undef BLR_B1_DHSUM
 #undef BLR_HLOAD
 #undef BLR_GLOAD
 #undef BLR_BLOAD
