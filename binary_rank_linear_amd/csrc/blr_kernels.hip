@@ -1315,10 +1315,194 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
     }
 }
 
+// The same contractions on 256x256 tiles, the tokens split into `splits`
+// ranges of tps tokens (a multiple of 32) so that the few large tiles still
+// fill the GPU; each range's partial sums are added to `out` atomically
+// (zeroed first unless the job accumulates). Per output element and token
+// this reads 8 bytes of activations for 256 + 256 products, half the bytes
+// per product of the 128x128 tiling. Blocks: job, then range, then tile, so
+// the tiles of one (job, range) run on one XCD and share their B rows and
+// their A columns in its L2. 8 waves in a 4x2 layout of 64x128 blocks; per
+// step of 32 tokens each thread stages a 4-token x 4-column block of both
+// operands (rounded to f16, transposed into LDS), two register stages ahead.
+constexpr int TN2_T = 256, TN2_LDK = 40, TN2_TP = 2;
+__global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int splits, int64_t tps) {
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][TN2_T * TN2_LDK];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TN2_T * TN2_LDK];
+    const int G = gridDim.x;
+    int b = (G % NUM_XCD == 0) ? (int)(blockIdx.x % NUM_XCD) * (G / NUM_XCD) + (int)(blockIdx.x / NUM_XCD)
+                               : (int)blockIdx.x;
+    int j = 0;
+    while (j + 1 < jobs.count && b >= jobs.job[j + 1].tiles_before) ++j;
+    const TnJob &jb = jobs.job[j];
+    b -= jb.tiles_before;
+    const int ntn = jb.No / TN2_T, tiles = (jb.Mo / TN2_T) * ntn;
+    const int sp = b / tiles, tl = b - sp * tiles;
+    const int mt = tl / ntn, nt = tl - mt * ntn;
+    const int m0 = mt * TN2_T, n0 = nt * TN2_T;
+    const int64_t T = jobs.T;
+    const int64_t tb0 = (int64_t)sp * tps;                       // first token of the range
+    const int64_t tend = tb0 + tps < T ? tb0 + tps : T;          // one past its last
+    if (tb0 >= tend) return;  // an empty range (uniform per workgroup)
+    const int64_t nk = (tend - tb0 + 31) / 32;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;  // 64 A columns x 128 B columns
+    // staging block: tokens 4*tq .. +3 of the step, columns 4*cq .. +3 of both tiles
+    const int tq = lane & 7, cq = wave * 8 + (lane >> 3);
+    f32x4_t csa, csb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        csa[e] = jb.acol[m0 + 4 * cq + e] * jb.ascale;
+        csb[e] = jb.bcol[n0 + 4 * cq + e] * jb.bscale;
+    }
+    const float *srca = jb.A + m0 + 4 * cq, *srcb = jb.B + n0 + 4 * cq;
+    const int wofs = 4 * cq * TN2_LDK + 4 * tq;
+    constexpr int BUFH = TN2_T * TN2_LDK;
+    f32x4_t ra[TN2_TP][4], rb[TN2_TP][4];
+#define TN2_LOAD(q, kt)                                                                    \
+    do {                                                                                   \
+        const int64_t k_ = (kt) < nk ? (kt) : nk - 1;                                      \
+        const int64_t t0_ = tb0 + k_ * 32 + 4 * tq;                                        \
+        if (tb0 + k_ * 32 + 32 <= tend) {                                                  \
+            _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                \
+                ra[q][e] = *reinterpret_cast<const f32x4_t *>(srca + (t0_ + e) * jb.lda);  \
+                rb[q][e] = *reinterpret_cast<const f32x4_t *>(srcb + (t0_ + e) * jb.ldb);  \
+            }                                                                              \
+        } else {                                                                           \
+            _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                \
+                const bool in_ = t0_ + e < tend;                                           \
+                const int64_t tc_ = in_ ? t0_ + e : tend - 1;                              \
+                const f32x4_t z_ = {0.f, 0.f, 0.f, 0.f};                                   \
+                const f32x4_t va_ = *reinterpret_cast<const f32x4_t *>(srca + tc_ * jb.lda); \
+                const f32x4_t vb_ = *reinterpret_cast<const f32x4_t *>(srcb + tc_ * jb.ldb); \
+                ra[q][e] = in_ ? va_ : z_;                                                 \
+                rb[q][e] = in_ ? vb_ : z_;                                                 \
+            }                                                                              \
+        }                                                                                  \
+    } while (0)
+#define TN2_STORE(q, buf)                                                                  \
+    do {                                                                                   \
+        _Pragma("unroll") for (int c_ = 0; c_ < 4; ++c_) {                                 \
+            uint2 ha_, hb_;                                                                \
+            ha_.x = f16x2_scaled(ra[q][0][c_], csa[c_], ra[q][1][c_], csa[c_]);            \
+            ha_.y = f16x2_scaled(ra[q][2][c_], csa[c_], ra[q][3][c_], csa[c_]);            \
+            hb_.x = f16x2_scaled(rb[q][0][c_], csb[c_], rb[q][1][c_], csb[c_]);            \
+            hb_.y = f16x2_scaled(rb[q][2][c_], csb[c_], rb[q][3][c_], csb[c_]);            \
+            *reinterpret_cast<uint2 *>(&As[buf][wofs + c_ * TN2_LDK]) = ha_;               \
+            *reinterpret_cast<uint2 *>(&Bs[buf][wofs + c_ * TN2_LDK]) = hb_;               \
+        }                                                                                  \
+    } while (0)
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < TN2_TP; ++q) TN2_LOAD(q, q);
+    TN2_STORE(0, 0);
+    TN2_LOAD(0, TN2_TP);
+    __syncthreads();
+    const int aro = (wm * 64 + (lane & 31)) * TN2_LDK + (lane >> 5) * 8;
+    const int bro = (wn * 128 + (lane & 31)) * TN2_LDK + (lane >> 5) * 8;
+    for (int64_t kt0 = 0; kt0 < nk; kt0 += TN2_TP) {
+#pragma unroll
+        for (int u = 0; u < TN2_TP; ++u) {
+            const int64_t kt = kt0 + u;
+            if (kt >= nk) break;  // uniform
+            const int cur = (int)(kt & 1);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                half8_t fa[2], fb[4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    fa[i] = *reinterpret_cast<const half8_t *>(&As[cur][aro + i * 32 * TN2_LDK + ks * 16]);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    fb[jj] = *reinterpret_cast<const half8_t *>(&Bs[cur][bro + jj * 32 * TN2_LDK + ks * 16]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+            }
+            TN2_STORE((u + 1) % TN2_TP, cur ^ 1);
+            TN2_LOAD((u + 1) % TN2_TP, kt + 1 + TN2_TP);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#undef TN2_LOAD
+#undef TN2_STORE
+    // out row m0 + wm*64 + i*32 + 8*(v/4) + 4*(lane/32) + v%4, column
+    // n0 + wn*128 + jj*32 + lane%32: one range stores (or accumulates), several add
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            float *o = jb.out + row * jb.No + n0 + wn * 128 + (lane & 31);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float val = acc[i][jj][v] * jb.oscale;
+                if (splits > 1) {
+                    unsafeAtomicAdd(o + jj * 32, val);
+                } else {
+                    o[jj * 32] = jb.acc ? o[jj * 32] + val : val;
+                }
+            }
+        }
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float *__restrict__ p, int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i + 4 <= n) {
+        *reinterpret_cast<f32x4_t *>(p + i) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
+        for (int64_t k = i; k < n; ++k) p[k] = 0.0f;
+    }
+}
+
 hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
+    if (jobs.T < 1) return hipErrorInvalidValue;
+    bool big = true;
+    for (int j = 0; j < jobs.count; ++j) {
+        if (jobs.job[j].Mo % TN_BM || jobs.job[j].No % TN_BN) return hipErrorInvalidValue;
+        if (jobs.job[j].Mo % TN2_T || jobs.job[j].No % TN2_T) big = false;
+    }
+    if (big) {
+        // tiles of all jobs, then as many token ranges (of at least 512
+        // tokens) as bring the workgroups to about 256
+        int tiles = 0;
+        for (int j = 0; j < jobs.count; ++j) tiles += (jobs.job[j].Mo / TN2_T) * (jobs.job[j].No / TN2_T);
+        const int64_t steps = (jobs.T + 31) / 32;
+        int splits = (256 + tiles - 1) / tiles;
+        if (splits > steps / 16) splits = (int)(steps / 16);
+        if (splits < 1) splits = 1;
+        const int64_t tps = ((steps + splits - 1) / splits) * 32;
+        int total = 0;
+        for (int j = 0; j < jobs.count; ++j) {
+            jobs.job[j].tiles_before = total;
+            total += (jobs.job[j].Mo / TN2_T) * (jobs.job[j].No / TN2_T) * splits;
+        }
+        prof_begin(K_GEMM_SIGNS, s);
+        if (splits > 1) {
+            for (int j = 0; j < jobs.count; ++j) {
+                if (jobs.job[j].acc) continue;
+                const int64_t n = (int64_t)jobs.job[j].Mo * jobs.job[j].No;
+                hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, s,
+                                   jobs.job[j].out, n);
+            }
+        }
+        hipLaunchKernelGGL(gemm_tn2_kernel, dim3((unsigned)total), dim3(512), 0, s, jobs, splits, tps);
+        hipError_t e = hipGetLastError();
+        prof_end(s);
+        return e;
+    }
     int total = 0;
     for (int j = 0; j < jobs.count; ++j) {
-        if (jobs.job[j].Mo % TN_BM || jobs.job[j].No % TN_BN || jobs.T < 1) return hipErrorInvalidValue;
         jobs.job[j].tiles_before = total;
         total += (jobs.job[j].Mo / TN_BM) * (jobs.job[j].No / TN_BN);
     }

@@ -77,6 +77,27 @@ def test_sign_grads_accumulate_and_c_tape(dev):
 
 
 @pytest.mark.gpu
+def test_sign_grads_accumulate_over_token_ranges(dev):
+    # d and r multiples of 256 and 35 steps of 32 tokens: the 256x256 tiles
+    # with the tokens split in two ranges whose partial sums are added
+    # atomically, onto the caller's values (accumulate) and onto zeros
+    M, d_in, d_out, r = 1100, 512, 256, 256
+    d = synth.custom(M, d_in, d_out, r, seed=23, dy_sigma=1e-6)
+    gs = float(d["gscale"])
+    rng = np.random.default_rng(4)
+    GU, GV = oracle.sign_grads(d["x"], d["dy"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"])
+    gu0 = rng.standard_normal(GU.shape) * np.abs(GU).mean()
+    gv0 = rng.standard_normal(GV.shape) * np.abs(GV).mean()
+    say("sign gradients over two token ranges, accumulate and overwrite")
+    _, _, _, _, gu, gv = run_signs(d, gs, dev, gu0=gu0, gv0=gv0, acc=True)
+    assert oracle.rel_frobenius(gu, gu0.astype(np.float32) + GU) < TOL
+    assert oracle.rel_frobenius(gv, gv0.astype(np.float32) + GV) < TOL
+    _, _, _, _, gu, gv = run_signs(d, gs, dev, gu0=gu0, gv0=gv0, acc=False)
+    assert oracle.rel_frobenius(gu, GU) < TOL
+    assert oracle.rel_frobenius(gv, GV) < TOL
+
+
+@pytest.mark.gpu
 def test_sign_grads_gscale_invariance_and_negative_control(dev):
     M, d_in, d_out, r = 256, 512, 512, 256
     d = synth.custom(M, d_in, d_out, r, seed=11, dy_sigma=1e-7)
