@@ -1356,29 +1356,33 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
         csa[e] = jb.acol[m0 + 4 * cq + e] * jb.ascale;
         csb[e] = jb.bcol[n0 + 4 * cq + e] * jb.bscale;
     }
-    const float *srca = jb.A + m0 + 4 * cq, *srcb = jb.B + n0 + 4 * cq;
+    // (the job's fields in registers: read from the argument block once)
+    const int64_t lda = jb.lda, ldb = jb.ldb;
+    const int No = jb.No, accf = jb.acc;
+    const float osc = jb.oscale;
+    float *const outp = jb.out;
     const int wofs = 4 * cq * TN2_LDK + 4 * tq;
     constexpr int BUFH = TN2_T * TN2_LDK;
     f32x4_t ra[TN2_TP][4], rb[TN2_TP][4];
+    // Buffer loads: a token row at or past T lies past the buffer's range
+    // and reads as zero (only the last range has a partial step; the others
+    // end on a multiple of 32 tokens); byte offsets of tokens 4 tq + e of the
+    // range's first step, advanced by whole steps
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(jb.A, (uint64_t)T * lda * 4);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(jb.B, (uint64_t)T * ldb * 4);
+    uint32_t oa[4], ob[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        oa[e] = (uint32_t)(((tb0 + 4 * tq + e) * lda + m0 + 4 * cq) * 4);
+        ob[e] = (uint32_t)(((tb0 + 4 * tq + e) * ldb + n0 + 4 * cq) * 4);
+    }
 #define TN2_LOAD(q, kt)                                                                    \
     do {                                                                                   \
-        const int64_t k_ = (kt) < nk ? (kt) : nk - 1;                                      \
-        const int64_t t0_ = tb0 + k_ * 32 + 4 * tq;                                        \
-        if (tb0 + k_ * 32 + 32 <= tend) {                                                  \
-            _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                \
-                ra[q][e] = *reinterpret_cast<const f32x4_t *>(srca + (t0_ + e) * jb.lda);  \
-                rb[q][e] = *reinterpret_cast<const f32x4_t *>(srcb + (t0_ + e) * jb.ldb);  \
-            }                                                                              \
-        } else {                                                                           \
-            _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                \
-                const bool in_ = t0_ + e < tend;                                           \
-                const int64_t tc_ = in_ ? t0_ + e : tend - 1;                              \
-                const f32x4_t z_ = {0.f, 0.f, 0.f, 0.f};                                   \
-                const f32x4_t va_ = *reinterpret_cast<const f32x4_t *>(srca + tc_ * jb.lda); \
-                const f32x4_t vb_ = *reinterpret_cast<const f32x4_t *>(srcb + tc_ * jb.ldb); \
-                ra[q][e] = in_ ? va_ : z_;                                                 \
-                rb[q][e] = in_ ? vb_ : z_;                                                 \
-            }                                                                              \
+        const uint32_t k_ = (uint32_t)((kt) < nk ? (kt) : nk - 1);                         \
+        const uint32_t sa_ = k_ * (uint32_t)(32 * lda * 4), sb_ = k_ * (uint32_t)(32 * ldb * 4); \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
+            ra[q][e] = load_f32x4(rA, oa[e] + sa_, 0u);                                    \
+            rb[q][e] = load_f32x4(rB, ob[e] + sb_, 0u);                                    \
         }                                                                                  \
     } while (0)
 #define TN2_STORE(q, buf)                                                                  \
@@ -1438,30 +1442,37 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
 #undef TN2_STORE
     // out row m0 + wm*64 + i*32 + 8*(v/4) + 4*(lane/32) + v%4, column
     // n0 + wn*128 + jj*32 + lane%32: one range stores (or accumulates), several add
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            float *o = jb.out + row * jb.No + n0 + wn * 128 + (lane & 31);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const float val = acc[i][jj][v] * jb.oscale;
-                if (splits > 1) {
-                    unsafeAtomicAdd(o + jj * 32, val);
-                } else {
-                    o[jj * 32] = jb.acc ? o[jj * 32] + val : val;
-                }
+    float *const o0 = outp + (int64_t)(m0 + wm * 64 + 4 * (lane >> 5)) * No + n0 + wn * 128 + (lane & 31);
+#define TN2_EPI(OP)                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                          \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v)                                     \
+            _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) {                             \
+                float *o = o0 + (int64_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * No + jj * 32; \
+                const float val = acc[i][jj][v] * osc;                                     \
+                OP;                                                                        \
             }
-        }
+    if (splits > 1) {
+        TN2_EPI(unsafeAtomicAdd(o, val))
+    } else if (accf) {
+        TN2_EPI(*o += val)
+    } else {
+        TN2_EPI(*o = val)
+    }
+#undef TN2_EPI
 }
 
-__global__ __launch_bounds__(256) void zero_f32_kernel(float *__restrict__ p, int64_t n) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i + 4 <= n) {
-        *reinterpret_cast<f32x4_t *>(p + i) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    } else {
-        for (int64_t k = i; k < n; ++k) p[k] = 0.0f;
+// zeroes the outputs of the jobs that do not accumulate (blockIdx.y = job)
+__global__ __launch_bounds__(256) void zero_outputs_kernel(TnJobs jobs) {
+    const TnJob &jb = jobs.job[blockIdx.y];
+    if (jb.acc) return;
+    const int64_t n = (int64_t)jb.Mo * jb.No;
+    float *const p = jb.out;
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * 1024) {
+        if (i + 4 <= n) {
+            *reinterpret_cast<f32x4_t *>(p + i) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
+            for (int64_t k = i; k < n; ++k) p[k] = 0.0f;
+        }
     }
 }
 
@@ -1488,14 +1499,8 @@ hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
             total += (jobs.job[j].Mo / TN2_T) * (jobs.job[j].No / TN2_T) * splits;
         }
         prof_begin(K_GEMM_SIGNS, s);
-        if (splits > 1) {
-            for (int j = 0; j < jobs.count; ++j) {
-                if (jobs.job[j].acc) continue;
-                const int64_t n = (int64_t)jobs.job[j].Mo * jobs.job[j].No;
-                hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, s,
-                                   jobs.job[j].out, n);
-            }
-        }
+        if (splits > 1 && !jobs.job[0].acc)  // (every job accumulates, or none)
+            hipLaunchKernelGGL(zero_outputs_kernel, dim3(1024, (unsigned)jobs.count), dim3(256), 0, s, jobs);
         hipLaunchKernelGGL(gemm_tn2_kernel, dim3((unsigned)total), dim3(512), 0, s, jobs, splits, tps);
         hipError_t e = hipGetLastError();
         prof_end(s);
