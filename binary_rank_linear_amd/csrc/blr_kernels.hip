@@ -219,6 +219,21 @@ __device__ __forceinline__ half8_t sign_frag(uint32_t w, uint32_t sel, uint32_t 
     return __builtin_bit_cast(half8_t, d);
 }
 
+// B fragment of -S times a column scale: h2 holds the column's f16 scale in
+// both halves; the sign bit XORed into it gives -S * scale exactly (one
+// v_bitop3 per dword on gfx950)
+__device__ __forceinline__ half8_t sign_frag_h(uint32_t w, uint32_t sel, uint32_t sgnmask, uint32_t h2) {
+    const uint32_t y = __builtin_amdgcn_perm(w, w, sel);
+    u32x4_t d;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const u16x2_t sh = {(uint16_t)(15 - 2 * q), (uint16_t)(14 - 2 * q)};
+        const u16x2_t t = __builtin_bit_cast(u16x2_t, y) << sh;
+        d[q] = (__builtin_bit_cast(uint32_t, t) & sgnmask) ^ h2;
+    }
+    return __builtin_bit_cast(half8_t, d);
+}
+
 // Bitmap transpose: out [r][rows/32] from bits [rows][r/32]. A wavefront
 // takes 64 rows x one word column (32 ranks): each lane loads its row's word,
 // then one wave-wide ballot per bit position gives, for rank 32w+b, the
@@ -872,9 +887,16 @@ static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
 // cross-wave sum: every wave holds all 64 rows of its columns.
 constexpr int AS_BM = 64, AS_BN = 256, AS_KMAX = 512;  // LDS: 64 x (K + 8) halves, 66.5 KB at K = 512
 
-template <int KG, int TPW, bool OUT, bool OUT2, bool DOT>
+// PR > 0: several paths along K, PR * 128 ranks each (K = paths * PR * 128),
+// the bitmap of path q at Bbits + q * b_pstride words ([N][PR * 4] words),
+// and out2 (+)= sum over paths of out2col_q . product_q: path q's column scale
+// (rounded to f16) is folded into its decoded signs, so one sweep over K
+// forms the sum (no column partials in this mode).
+template <int KG, int TPW, bool OUT, bool OUT2, bool DOT, int PR = 0>
 __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_n) {
     constexpr int K = 128 * KG, LDK = K + 8;
+    static_assert(PR == 0 || (OUT2 && !OUT && !DOT && KG % PR == 0), "paths folded along K");
+    constexpr int NP = PR ? KG / PR : 1;  // paths
     __shared__ __attribute__((aligned(16))) _Float16 As[AS_BM * LDK];
     constexpr int FM = 2, FN = 2, TN = 64;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -890,14 +912,16 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
     // bitmap words of this lane's two plane rows in each tile, KG 16-byte
     // groups per row; tile 0's first (they arrive while the block is
     // staged), each later tile's at the start of the one before
-    constexpr int KW = K / 32;  // bitmap words per plane row
+    constexpr int KW = PR ? PR * 4 : K / 32;  // bitmap words per plane row (of a path)
     u32x4_t wall[TPW][2][KG];
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.Bbits, (uint64_t)N * K / 8);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.Bbits, PR ? (uint64_t)(NP - 1) * p.b_pstride * 4 + (uint64_t)N * KW * 4
+                                                            : (uint64_t)N * K / 8);
 #define AS_WLOAD(tt)                                                                       \
     do {                                                                                   \
         _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                    \
             const uint32_t bo_ = (uint32_t)(((t0 + (tt)) * AS_BN + wn * 64 + j * 32 + (lane & 31)) * KW * 4); \
-            _Pragma("unroll") for (int g = 0; g < KG; ++g) wall[tt][j][g] = load_u32x4(rB, bo_, (uint32_t)g * 16); \
+            _Pragma("unroll") for (int g = 0; g < KG; ++g) wall[tt][j][g] = load_u32x4(rB, bo_, \
+                PR ? (uint32_t)((g / (PR ? PR : 1)) * p.b_pstride * 4 + (g % (PR ? PR : 1)) * 16) : (uint32_t)g * 16); \
         }                                                                                  \
     } while (0)
     AS_WLOAD(0);
@@ -906,11 +930,21 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
     // columns 4 (i % (K/4)); rows past M read row M-1 (never stored or summed).
     // The column scales of the epilogue (OUT2) for every tile, first.
     float c2all[TPW][FN];
+    uint32_t h2all[PR ? TPW : 1][PR ? FN : 1][NP];  // PR: each path's f16 column scale, both halves
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            c2all[tt][j] = OUT2 ? p.out2col[(t0 + tt) * AS_BN + wn * TN + j * 32 + (lane & 31)] : 0.0f;
+        for (int j = 0; j < FN; ++j) {
+            const int n_ = (t0 + tt) * AS_BN + wn * TN + j * 32 + (lane & 31);
+            c2all[tt][j] = (OUT2 && !PR) ? p.out2col[n_] : 1.0f;
+            if (PR) {
+#pragma unroll
+                for (int q = 0; q < NP; ++q) {
+                    const uint32_t h_ = __builtin_bit_cast(uint16_t, (_Float16)p.out2col[q * p.o2_pstride + n_]);
+                    h2all[PR ? tt : 0][PR ? j : 0][q] = h_ | (h_ << 16);
+                }
+            }
+        }
     {
         // all of a thread's chunks in flight at once (up to 32 float4); when
         // 256 is a multiple of the chunks per row, a thread's chunks share
@@ -1028,7 +1062,9 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
         do {                                                                               \
             _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[buf][i] =                    \
                 *reinterpret_cast<const half8_t *>(arow + i * 32 * LDK + 16 * (kb));       \
-            _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[buf][j] =                    \
+            _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[buf][j] = PR ?               \
+                sign_frag_h(wall[tt][j][(kb) / 8][((kb) / 2) % 4], sel[(kb) % 2], sgnmask,  \
+                            h2all[PR ? tt : 0][PR ? j : 0][(kb) / (8 * (PR ? PR : 1))]) :  \
                 sign_frag(wall[tt][j][(kb) / 8][((kb) / 2) % 4], sel[(kb) % 2], sgnmask, one16); \
         } while (0)
         AS_FRAGS(0, 0);
@@ -1100,19 +1136,19 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
 #undef AS_WLOAD
 }
 
-template <int KG, int TPW, bool OUT, bool OUT2, bool DOT>
+template <int KG, int TPW, bool OUT, bool OUT2, bool DOT, int PR = 0>
 static hipError_t launch_gemm_as_tt(int id, const GemmArgs &a, hipStream_t s) {
     const int64_t mtiles = (a.M + AS_BM - 1) / AS_BM;
     const int64_t gn = a.N / AS_BN / TPW;
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_as_kernel<KG, TPW, OUT, OUT2, DOT>), dim3((unsigned)(mtiles * gn)), dim3(256), 0, s, a,
-                       (int)gn);
+    hipLaunchKernelGGL((gemm_as_kernel<KG, TPW, OUT, OUT2, DOT, PR>), dim3((unsigned)(mtiles * gn)), dim3(256), 0, s,
+                       a, (int)gn);
     hipError_t e = hipGetLastError();
     prof_end(s);
     return e;
 }
 
-template <int KG, bool OUT, bool OUT2, bool DOT>
+template <int KG, bool OUT, bool OUT2, bool DOT, int PR = 0>
 static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
     if (a.N % AS_BN != 0 || a.K != 128 * KG) return hipErrorInvalidValue;
     const int64_t mtiles = (a.M + AS_BM - 1) / AS_BM;
@@ -1121,9 +1157,9 @@ static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
     // that still gives about two workgroups per CU; the runs of one M tile
     // land on one XCD
     if (KG <= 4 && ntiles % 4 == 0 && mtiles * (ntiles / 4) >= 512)
-        return launch_gemm_as_tt<KG, 4, OUT, OUT2, DOT>(id, a, s);
-    if (ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 512) return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT>(id, a, s);
-    return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT>(id, a, s);
+        return launch_gemm_as_tt<KG, 4, OUT, OUT2, DOT, PR>(id, a, s);
+    if (ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 512) return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT, PR>(id, a, s);
+    return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT, PR>(id, a, s);
 }
 
 template <bool OUT, bool OUT2, bool DOT>
@@ -1178,6 +1214,16 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s);
         case GEMM_PLANE: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4, true>(K_GEMM_PLANE, a, s);
         case GEMM_F2_MP:
+            // the held-activation kernel with each path's h folded into its
+            // signs, when the paths' ranks fit it; else one flush per path
+            if (as && a.N % AS_BN == 0 && (a.path_k == 128 || a.path_k == 256)) {
+                switch (a.K / 128 * 10 + a.path_k / 128) {
+                    case 21: return launch_gemm_as_t<2, false, true, false, 1>(K_GEMM_F2, a, s);
+                    case 31: return launch_gemm_as_t<3, false, true, false, 1>(K_GEMM_F2, a, s);
+                    case 41: return launch_gemm_as_t<4, false, true, false, 1>(K_GEMM_F2, a, s);
+                    case 42: return launch_gemm_as_t<4, false, true, false, 2>(K_GEMM_F2, a, s);
+                }
+            }
             return launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, false, 8, false, 4, false, true>(K_GEMM_F2, a, s);
         case GEMM_B2_MP:
             return launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8, false, 4, false, true>(K_GEMM_B2, a, s);

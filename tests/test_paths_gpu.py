@@ -22,6 +22,8 @@ SHAPES = [
     (513, 1024, 256, 512, 2),  # two rank tiles per path in the fused dh launch
     (200, 384, 256, 384, 2),   # dh from c recomputed per path (no fused launch at r = 384)
     (70, 256, 256, 128, 4),    # the most paths, the page's 70 tokens
+    (300, 256, 512, 256, 2),   # F2 on the held activation, each path's h folded into its signs (256 ranks a path)
+    (130, 512, 768, 128, 3),   # the same with 128 ranks a path, three paths
 ]
 
 
@@ -88,10 +90,11 @@ def test_paths_sign_grads(dev):
 
 
 @pytest.mark.gpu
-def test_paths_accumulate_rules(dev):
-    """y += sum_p h_p.c_p and dx += sum_p g_p.dx'_p when asked."""
-    M, d_in, d_out, r, P = 200, 256, 384, 128, 3
-    d = synth.custom_paths(M, d_in, d_out, r, P, seed=8202, dy_sigma=1e-6)
+@pytest.mark.parametrize("M,d_in,d_out,r,P", [(200, 256, 384, 128, 3), (200, 256, 512, 256, 2)])
+def test_paths_accumulate_rules(dev, M, d_in, d_out, r, P):
+    """y += sum_p h_p.c_p and dx += sum_p g_p.dx'_p when asked (the second
+    shape takes the held-activation F2 with the paths' h folded in)."""
+    d = synth.custom_paths(M, d_in, d_out, r, P, seed=8202 + r, dy_sigma=1e-6)
     R = np.random.default_rng(5)
     y0 = R.standard_normal((M, d_out)).astype(np.float32)
     dx0 = (R.standard_normal((M, d_in)) * 1e-5).astype(np.float32)
