@@ -57,6 +57,8 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
         return kernel_work("gemm_b2_dbl_svt", w)
     if name == "gemm_sign_grads":    # read dy, a, x, db; write G_U, G_V
         return M * (do + di + 2 * r) * f32 + (do + di) * r * f32, 2.0 * M * r * (do + di)
+    if name == "sign_grads_zero":    # zero G_U, G_V before the token ranges add into them
+        return (do + di) * r * f32, 0.0
     if name == "colsum_dy_c":        # read dy and c
         return 2.0 * M * do * f32, 2.0 * M * do
     if name == "transpose_bits":     # one bitmap in, its transpose out (average of U and V)
