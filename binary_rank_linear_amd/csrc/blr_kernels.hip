@@ -280,7 +280,14 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     constexpr int NT = WM * WN * 64;  // threads of the contraction role
     constexpr int BK = 16 * KB;     // k per step: KB MFMA k-blocks, KB/2 bitmap words per plane row
     constexpr int U = 8 / KB;       // steps per group of 4 bitmap words (the loop unroll)
-    constexpr int LDK = BK + 8;     // halves per LDS row (pad: conflict-free 16-byte reads)
+    // halves per LDS row of the f16 activation tile. At BK = 64 a pad of 8
+    // makes the stagers' 8-byte writes and the fragments' 16-byte reads
+    // conflict-free; at BK = 32 (8 threads a row) no pitch does both, so the
+    // rows are unpadded and a row's 16-byte chunks are permuted: chunk c of
+    // row m sits at chunk c ^ ((m >> 2) & 3) (both conflict-free on gfx950,
+    // measured)
+    constexpr bool ASW = BK == 32;
+    constexpr int LDK = ASW ? BK : BK + 8;
     constexpr int NS = 3;           // LDS ring depth
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -375,8 +382,14 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.Bbits, PLANE ? 0 : (uint64_t)N * K / 8);
     const __amdgpu_buffer_rsrc_t rP = make_rsrc(p.Bplane, PLANE ? (uint64_t)N * K * 2 : 0);
     const uint32_t coff = (uint32_t)c4 * 16;
-    const int wofs = arow * LDK + c4 * 4;                                   // LDS write, halves
-    const int rofs = (wm * TM + (lane & 31)) * LDK + (lane >> 5) * 8;      // fragment read, halves
+    // LDS write (halves); rows arow + v RPP share the permutation (RPP is a
+    // multiple of 16 wherever BK = 32)
+    const int wofs = arow * LDK + (ASW ? 8 * ((c4 >> 1) ^ ((arow >> 2) & 3)) + 4 * (c4 & 1) : c4 * 4);
+    // fragment reads (halves) of k-block s: 8 halves at k = 8 (lane / 32) + 16 s
+    const int rrow_ = wm * TM + (lane & 31);
+    const int rofs = rrow_ * LDK + (ASW ? 8 * ((lane >> 5) ^ ((rrow_ >> 2) & 3)) : (lane >> 5) * 8);
+    const int rofs1 = rrow_ * LDK + (ASW ? 8 * (((lane >> 5) + 2) ^ ((rrow_ >> 2) & 3)) : (lane >> 5) * 8 + 16);
+    static_assert(!ASW || (RPP % 16 == 0 && KB == 2), "permuted activation tile");
     // Bitmap words of this lane's plane rows (one per 32-column block)
     uint32_t boff[FN];
 #pragma unroll
@@ -488,10 +501,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
 
 #define BLR_AFRAG(dst, buf)                                                                \
     do {                                                                                   \
-        const _Float16 *src_ = As + (buf) * (BM * LDK) + rofs;                             \
+        const _Float16 *src_ = As + (buf) * (BM * LDK);                                    \
         _Pragma("unroll") for (int i = 0; i < FM; ++i)                                     \
             _Pragma("unroll") for (int s = 0; s < KB; ++s) dst[i][s] =                     \
-                *reinterpret_cast<const half8_t *>(src_ + i * 32 * LDK + s * 16);          \
+                *reinterpret_cast<const half8_t *>(src_ + i * 32 * LDK +                   \
+                                                   (s == 0 ? rofs : s == 1 ? rofs1 : rofs + s * 16)); \
     } while (0)
 
 #define BLR_BFRAG(dst, words, u, kstep)                                                    \
