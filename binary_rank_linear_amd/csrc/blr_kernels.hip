@@ -1264,7 +1264,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
 // ahead; two LDS buffers; tokens past T are zero (only the last step checks).
 // The 8 waves multiply in a 4x2 layout of 32x64 blocks. One launch serves
 // both gradients.
-constexpr int TN_BM = 128, TN_BN = 128, TN_LDK = 40;
+constexpr int TN_BM = 128, TN_BN = 128, TN_LDK = 32;
 __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
     __shared__ __attribute__((aligned(16))) _Float16 As[2][TN_BM * TN_LDK];
     __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TN_BN * TN_LDK];
@@ -1285,8 +1285,10 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;   // 32-row x 64-column MMA block
     const bool bside = wave >= 4;              // stages B (else A)
-    // staging block: tokens 4*tb .. +3 of the step, columns 4*cb .. +3 of the tile
-    const int tb = lane & 7, cb = (wave & 3) * 8 + (lane >> 3);
+    // staging block: tokens 4*tb .. +3 of the step, columns 4*cb .. +3 of the
+    // tile; consecutive lanes take consecutive column groups of one token row,
+    // so each group of lanes reads whole 128-byte lines
+    const int tb = lane >> 3, cb = (wave & 3) * 8 + (lane & 7);
     const float *col = bside ? jb.bcol + n0 : jb.acol + m0;
     const float sc = bside ? jb.bscale : jb.ascale;
     f32x4_t cs;
@@ -1294,7 +1296,10 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
     for (int e = 0; e < 4; ++e) cs[e] = col[4 * cb + e] * sc;
     const int64_t ld = bside ? jb.ldb : jb.lda;
     const float *src = (bside ? jb.B + n0 : jb.A + m0) + 4 * cb;
-    _Float16 *dst0 = (bside ? &Bs[0][0] : &As[0][0]) + 4 * cb * TN_LDK + 4 * tb;
+    // the tiles are [column][32 tokens] f16 with no pad; the 8-token chunk c of
+    // column n sits at chunk c ^ ((n >> 2) & 3) (two passes for the 8-byte
+    // writes, conflict-free 16-byte fragment reads)
+    _Float16 *dst0 = (bside ? &Bs[0][0] : &As[0][0]) + 4 * cb * TN_LDK + 8 * ((tb >> 1) ^ (cb & 3)) + 4 * (tb & 1);
     constexpr int BUFH = TN_BM * TN_LDK;  // halves per buffer (A and B alike)
     const int64_t nk = (T + 31) / 32;
     constexpr int TP = 4;
@@ -1334,8 +1339,9 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
     TN_STORE(0, 0);
     TN_LOAD(0, TP);
     __syncthreads();
-    const int aro = (wm * 32 + (lane & 31)) * TN_LDK + (lane >> 5) * 8;
-    const int bro = (wn * 64 + (lane & 31)) * TN_LDK + (lane >> 5) * 8;
+    const int fsw = (lane >> 2) & 3;  // the permutation of the lane's columns
+    const int aro = (wm * 32 + (lane & 31)) * TN_LDK;
+    const int bro = (wn * 64 + (lane & 31)) * TN_LDK;
     for (int64_t kt0 = 0; kt0 < nk; kt0 += TP) {
 #pragma unroll
         for (int u = 0; u < TP; ++u) {
@@ -1344,11 +1350,12 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
             const int cur = (int)(kt & 1);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const half8_t fa = *reinterpret_cast<const half8_t *>(&As[cur][aro + s * 16]);
+                const int ko = 8 * (((lane >> 5) + 2 * s) ^ fsw);
+                const half8_t fa = *reinterpret_cast<const half8_t *>(&As[cur][aro + ko]);
                 half8_t fb[2];
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
-                    fb[jj] = *reinterpret_cast<const half8_t *>(&Bs[cur][bro + jj * 32 * TN_LDK + s * 16]);
+                    fb[jj] = *reinterpret_cast<const half8_t *>(&Bs[cur][bro + jj * 32 * TN_LDK + ko]);
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
                     acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb[jj], acc[jj], 0, 0, 0);
@@ -1385,7 +1392,7 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
 // their A columns in its L2. 8 waves in a 4x2 layout of 64x128 blocks; per
 // step of 32 tokens each thread stages a 4-token x 4-column block of both
 // operands (rounded to f16, transposed into LDS), two register stages ahead.
-constexpr int TN2_T = 256, TN2_LDK = 40, TN2_TP = 2;
+constexpr int TN2_T = 256, TN2_LDK = 32, TN2_TP = 2;
 __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int splits, int64_t tps) {
     __shared__ __attribute__((aligned(16))) _Float16 As[2][TN2_T * TN2_LDK];
     __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TN2_T * TN2_LDK];
@@ -1408,8 +1415,10 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;  // 64 A columns x 128 B columns
-    // staging block: tokens 4*tq .. +3 of the step, columns 4*cq .. +3 of both tiles
-    const int tq = lane & 7, cq = wave * 8 + (lane >> 3);
+    // staging block: tokens 4*tq .. +3 of the step, columns 4*cq .. +3 of both
+    // tiles; consecutive lanes take consecutive column groups of one token row,
+    // so each group of lanes reads whole 128-byte lines
+    const int tq = lane >> 3, cq = wave * 8 + (lane & 7);
     f32x4_t csa, csb;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1421,7 +1430,11 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
     const int No = jb.No, accf = jb.acc;
     const float osc = jb.oscale;
     float *const outp = jb.out;
-    const int wofs = 4 * cq * TN2_LDK + 4 * tq;
+    // the tiles are [column][32 tokens] f16 with no pad; the 8-token chunk c of
+    // column n sits at chunk c ^ ((n >> 2) & 3), which keeps the stagers'
+    // 8-byte writes at two passes and the fragments' 16-byte reads
+    // conflict-free on gfx950 (measured)
+    const int wofs = 4 * cq * TN2_LDK + 8 * ((tq >> 1) ^ (cq & 3)) + 4 * (tq & 1);
     constexpr int BUFH = TN2_T * TN2_LDK;
     f32x4_t ra[TN2_TP][4], rb[TN2_TP][4];
     // Buffer loads: a token row at or past T lies past the buffer's range
@@ -1469,8 +1482,9 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
     TN2_STORE(0, 0);
     TN2_LOAD(0, TN2_TP);
     __syncthreads();
-    const int aro = (wm * 64 + (lane & 31)) * TN2_LDK + (lane >> 5) * 8;
-    const int bro = (wn * 128 + (lane & 31)) * TN2_LDK + (lane >> 5) * 8;
+    const int fsw = (lane >> 2) & 3;  // the permutation of the lane's columns
+    const int aro = (wm * 64 + (lane & 31)) * TN2_LDK;
+    const int bro = (wn * 128 + (lane & 31)) * TN2_LDK;
     for (int64_t kt0 = 0; kt0 < nk; kt0 += TN2_TP) {
 #pragma unroll
         for (int u = 0; u < TN2_TP; ++u) {
@@ -1482,10 +1496,12 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
                 half8_t fa[2], fb[4];
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    fa[i] = *reinterpret_cast<const half8_t *>(&As[cur][aro + i * 32 * TN2_LDK + ks * 16]);
+                    fa[i] = *reinterpret_cast<const half8_t *>(
+                        &As[cur][aro + i * 32 * TN2_LDK + 8 * (((lane >> 5) + 2 * ks) ^ fsw)]);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    fb[jj] = *reinterpret_cast<const half8_t *>(&Bs[cur][bro + jj * 32 * TN2_LDK + ks * 16]);
+                    fb[jj] = *reinterpret_cast<const half8_t *>(
+                        &Bs[cur][bro + jj * 32 * TN2_LDK + 8 * (((lane >> 5) + 2 * ks) ^ fsw)]);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
