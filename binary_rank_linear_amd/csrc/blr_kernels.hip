@@ -1176,6 +1176,242 @@ static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
     return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT, PR>(id, a, s);
 }
 
+// B2 of a layer of NP paths on the held activation block (K = NP paths of
+// 128 KGP ranks, the paths' db side by side): per output tile each path's
+// product is formed in turn from its own ranks (its accumulators restarting
+// from zero), its dot with the tile's x goes to that path's column partials,
+// and its g_p-scaled value is added to the tile's dx sum, which is stored
+// once after the last path. Each path's words are loaded while the path
+// before it runs. One workgroup per CU (the block of K <= 1024 ranks takes
+// up to 129 KB of LDS), each walking a run of tpw consecutive tiles; the
+// tile loop is not unrolled.
+template <int KGP, int NP>
+__global__ __launch_bounds__(256, 1) void gemm_as_paths_kernel(GemmArgs p, int groups_n, int tpw) {
+    constexpr int KG = KGP * NP, K = 128 * KG, LDK = K + 8;
+    static_assert(K <= 1024 && NP >= 2, "paths block");
+    __shared__ __attribute__((aligned(16))) _Float16 As[AS_BM * LDK];
+    constexpr int FM = 2, FN = 2, TN = 64, NKB = 8 * KGP;  // k-blocks per path
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = p.N;
+    const int64_t M = p.M;
+    const int L = blockIdx.x, G = gridDim.x;
+    const int T = (G % NUM_XCD == 0) ? (L % NUM_XCD) * (G / NUM_XCD) + L / NUM_XCD : L;
+    const int mt = T / groups_n, gn = T - mt * groups_n;
+    const int t0 = gn * tpw;
+    const int64_t m0 = (int64_t)mt * AS_BM;
+
+    // bitmap words of path q for this lane's two plane rows of tile t: KGP
+    // 16-byte groups per row, path q at Bbits + q * b_pstride words
+    u32x4_t w[2][2][KGP];
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc(p.Bbits, (uint64_t)(NP - 1) * p.b_pstride * 4 + (uint64_t)N * KGP * 16);
+#define ASP_WLOAD(buf, t_, q_)                                                             \
+    do {                                                                                   \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                    \
+            const uint32_t bo_ = (uint32_t)(((t_) * AS_BN + wn * 64 + j * 32 + (lane & 31)) * KGP * 16); \
+            _Pragma("unroll") for (int g = 0; g < KGP; ++g) w[buf][j][g] =                 \
+                load_u32x4(rB, bo_, (uint32_t)((q_) * p.b_pstride * 4 + g * 16));          \
+        }                                                                                  \
+    } while (0)
+    ASP_WLOAD(0, t0, 0);
+
+    // Stage the block, as the single-path kernel does: chunk i (float4) is
+    // row i / (K/4), columns 4 (i % (K/4)); rows past M read row M-1. When
+    // 256 is a multiple of the chunks per row, a thread's chunks share one
+    // column group and its scales are loaded once.
+    {
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)M * p.lda * 4);
+        const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.colscale, (uint64_t)K * 4);
+        constexpr int cpr = K / 4, nch = AS_BM * cpr;
+        constexpr int UNR = 16;
+        constexpr bool onecol = 256 % cpr == 0;
+        const f32x4_t c1 = onecol ? load_f32x4(rC, (uint32_t)(16 * (tid % cpr)), 0u) * p.ascale : f32x4_t{};
+        for (int i0 = 0; i0 < nch; i0 += 256 * UNR) {
+            f32x4_t v[UNR], c[onecol ? 1 : UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int i = i0 + u * 256 + tid;
+                const int ic = i < nch ? i : nch - 1;
+                const int row = ic / cpr, c4 = ic - row * cpr;
+                int64_t gm = m0 + row;
+                gm = gm < M ? gm : M - 1;
+                v[u] = load_f32x4(rA, (uint32_t)((gm * p.lda + 4 * c4) * 4), 0u);
+                if (!onecol) c[u] = load_f32x4(rC, (uint32_t)(16 * c4), 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int i = i0 + u * 256 + tid;
+                if (i < nch) {
+                    const int row = i / cpr, c4 = i - row * cpr;
+                    const f32x4_t cs = onecol ? c1 : c[onecol ? 0 : u] * p.ascale;
+                    uint2 h;
+                    h.x = f16x2_scaled(v[u].x, cs.x, v[u].y, cs.y);
+                    h.y = f16x2_scaled(v[u].z, cs.z, v[u].w, cs.w);
+                    *reinterpret_cast<uint2 *>(As + row * LDK + 4 * c4) = h;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const uint32_t grp = (uint32_t)(lane >> 5);
+    const uint32_t sel[2] = {grp * 0x01010101u, (2u + grp) * 0x01010101u};
+    uint32_t sgnmask, one16;
+    asm volatile("v_mov_b32 %0, 0x80008000" : "=v"(sgnmask));
+    asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one16));
+    const _Float16 *arow = As + (lane & 31) * LDK + (lane >> 5) * 8;  // fragment read base
+    const float osc = -p.oscale;  // decoded fragments hold -S
+    const uint64_t obytes = (uint64_t)M * N * 4;
+    const __amdgpu_buffer_rsrc_t rO2 = make_rsrc(p.out2, obytes);
+    const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.dot_other, obytes);
+    const int64_t rl = m0 + 4 * (lane >> 5);
+    const bool full = m0 + AS_BM <= M;
+
+    for (int tt = 0; tt < tpw; ++tt) {
+        const int t = t0 + tt;
+        int Nl = N;
+        asm volatile("" : "+s"(Nl));
+        const int cb = t * AS_BN + wn * TN + (lane & 31);
+        const uint32_t loff = (uint32_t)((rl * Nl + cb) * 4);
+#define ASP_UOFF(i, v, j) ((uint32_t)((8 * ((v) >> 2) + ((v) & 3)) * Ni + (j) * 32) * 4u)
+        // the tile's x (the dot operand of every path), loaded before the
+        // first path's MFMAs
+        float oth[FM][FN][16];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            int Ni = Nl;
+            asm volatile("" : "+s"(Ni));
+            const uint32_t lo_ = loff + (uint32_t)(i * 32 * Ni * 4);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const bool in_ = full || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) oth[i][j][v] = in_ ? load_f32_nt(rD, lo_, ASP_UOFF(i, v, j)) : 0.0f;
+            }
+        }
+        f32x16_t ysum[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) ysum[i][j][v] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            // the next path's words (this tile's, or the next tile's first)
+            if (q + 1 < NP) {
+                ASP_WLOAD((q + 1) & 1, t, q + 1);
+            } else if (tt + 1 < tpw) {
+                ASP_WLOAD((q + 1) & 1, t + 1, 0);
+            }
+            float c2[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) c2[j] = p.out2col[(int64_t)q * p.o2_pstride + cb + j * 32];
+            f32x16_t acc[FM][FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+            half8_t fa[2][FM], fb[2][FN];
+#define ASP_FRAGS(buf, kb)                                                                 \
+            do {                                                                           \
+                _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[buf][i] =                \
+                    *reinterpret_cast<const half8_t *>(arow + i * 32 * LDK + q * (128 * KGP) + 16 * (kb)); \
+                _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[buf][j] =                \
+                    sign_frag(w[q & 1][j][(kb) / 8][((kb) / 2) % 4], sel[(kb) % 2], sgnmask, one16); \
+            } while (0)
+            ASP_FRAGS(0, 0);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                if (kb + 1 < NKB) ASP_FRAGS((kb + 1) & 1, kb + 1);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[kb & 1][i], fb[kb & 1][j], acc[i][j], 0, 0, 0);
+                if (kb + 1 < NKB) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, FM, 0);
+#pragma unroll
+                    for (int m_ = 0; m_ < FM * FN; ++m_) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#undef ASP_FRAGS
+            // this path's product: its dot with x (rows past M hold zero x)
+            // and its g_p-scaled share of dx
+            float ds[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) ds[j] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const float val = acc[i][j][v] * osc;
+                        ds[j] += val * oth[i][j][v];
+                        ysum[i][j][v] += val * c2[j];
+                    }
+            // lanes l and l+32 hold other rows of the same column
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const float sum = ds[j] + __shfl_xor(ds[j], 32);
+                if (lane < 32) p.dot_partial[(int64_t)q * p.dot_pstride + (int64_t)mt * N + cb + j * 32] = sum;
+            }
+        }
+        if (NP & 1) {  // the next tile's first words arrived in buffer 1
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int g = 0; g < KGP; ++g) w[0][j][g] = w[1][j][g];
+        }
+        // dx (+)= the sum over paths, one row block at a time
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            int Ni = Nl;
+            asm volatile("" : "+s"(Ni));
+            const uint32_t lo_ = loff + (uint32_t)(i * 32 * Ni * 4);
+            float old[FN][16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const bool in_ = full || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) old[j][v] = (p.out2acc && in_) ? load_f32(rO2, lo_, ASP_UOFF(i, v, j)) : 0.0f;
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if (full || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) store_f32_nt(rO2, lo_, ASP_UOFF(i, v, j), old[j][v] + ysum[i][j][v]);
+                }
+        }
+#undef ASP_UOFF
+    }
+#undef ASP_WLOAD
+}
+
+template <int KGP, int NP>
+static hipError_t launch_gemm_as_paths_t(int id, const GemmArgs &a, hipStream_t s) {
+    const int64_t mtiles = (a.M + AS_BM - 1) / AS_BM;
+    const int ntiles = a.N / AS_BN;
+    // the longest run of tiles that still gives every CU a workgroup
+    int tpw = 1;
+    while (tpw * 2 <= 8 && ntiles % (tpw * 2) == 0 && mtiles * (ntiles / (tpw * 2)) >= 256) tpw *= 2;
+    const int64_t gn = ntiles / tpw;
+    prof_begin(id, s);
+    hipLaunchKernelGGL((gemm_as_paths_kernel<KGP, NP>), dim3((unsigned)(mtiles * gn)), dim3(256), 0, s, a, (int)gn,
+                       tpw);
+    hipError_t e = hipGetLastError();
+    prof_end(s);
+    return e;
+}
+
 template <bool OUT, bool OUT2, bool DOT>
 static hipError_t launch_gemm_as(int id, const GemmArgs &a, hipStream_t s) {
     switch (a.K) {
@@ -1240,6 +1476,20 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
             }
             return launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, false, 8, false, 4, false, true>(K_GEMM_F2, a, s);
         case GEMM_B2_MP:
+            // the held-activation kernel, each path's product in turn, when
+            // the paths' ranks fit its block; else one flush per path
+            if (wide && a.K <= 1024 && a.path_k % 128 == 0) {
+                switch (a.K / 128 * 10 + a.path_k / 128) {
+                    case 21: return launch_gemm_as_paths_t<1, 2>(K_GEMM_B2, a, s);
+                    case 31: return launch_gemm_as_paths_t<1, 3>(K_GEMM_B2, a, s);
+                    case 41: return launch_gemm_as_paths_t<1, 4>(K_GEMM_B2, a, s);
+                    case 42: return launch_gemm_as_paths_t<2, 2>(K_GEMM_B2, a, s);
+                    case 62: return launch_gemm_as_paths_t<2, 3>(K_GEMM_B2, a, s);
+                    case 63: return launch_gemm_as_paths_t<3, 2>(K_GEMM_B2, a, s);
+                    case 82: return launch_gemm_as_paths_t<2, 4>(K_GEMM_B2, a, s);
+                    case 84: return launch_gemm_as_paths_t<4, 2>(K_GEMM_B2, a, s);
+                }
+            }
             return launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, true, 8, false, 4, false, true>(K_GEMM_B2, a, s);
         case GEMM_B1_DH:
             switch (a.path_n ? a.path_n : a.N) {  // 64 tokens x up to 256 ranks of one path, 64 per wave

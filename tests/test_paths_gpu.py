@@ -24,6 +24,8 @@ SHAPES = [
     (70, 256, 256, 128, 4),    # the most paths, the page's 70 tokens
     (300, 256, 512, 256, 2),   # F2 on the held activation, each path's h folded into its signs (256 ranks a path)
     (130, 512, 768, 128, 3),   # the same with 128 ranks a path, three paths
+    (150, 512, 256, 384, 2),   # B2 on the held activation with 384 ranks a path
+    (100, 256, 256, 256, 4),   # four paths of 256 ranks: a 1024-rank block in one workgroup
 ]
 
 
@@ -90,10 +92,12 @@ def test_paths_sign_grads(dev):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("M,d_in,d_out,r,P", [(200, 256, 384, 128, 3), (200, 256, 512, 256, 2)])
+@pytest.mark.parametrize("M,d_in,d_out,r,P", [(200, 256, 384, 128, 3), (200, 256, 512, 256, 2),
+                                               (130, 512, 256, 512, 2)])
 def test_paths_accumulate_rules(dev, M, d_in, d_out, r, P):
-    """y += sum_p h_p.c_p and dx += sum_p g_p.dx'_p when asked (the second
-    shape takes the held-activation F2 with the paths' h folded in)."""
+    """y += sum_p h_p.c_p and dx += sum_p g_p.dx'_p when asked. Every shape
+    takes the held-activation B2 over the paths in turn; the first two the
+    held-activation F2 with the paths' h folded in, the third the generic F2."""
     d = synth.custom_paths(M, d_in, d_out, r, P, seed=8202 + r, dy_sigma=1e-6)
     R = np.random.default_rng(5)
     y0 = R.standard_normal((M, d_out)).astype(np.float32)
