@@ -1182,15 +1182,18 @@ static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
 // from zero), its dot with the tile's x goes to that path's column partials,
 // and its g_p-scaled value is added to the tile's dx sum, which is stored
 // once after the last path. Each path's words are loaded while the path
-// before it runs. One workgroup per CU (the block of K <= 1024 ranks takes
-// up to 129 KB of LDS), each walking a run of tpw consecutive tiles; the
-// tile loop is not unrolled.
+// before it runs, and the next tile's x while its last path runs. One
+// workgroup of 8 waves per CU (the block of K <= 1024 ranks takes up to
+// 129 KB of LDS), each walking a run of tpw consecutive tiles; the tile loop
+// is not unrolled.
 template <int KGP, int NP>
-__global__ __launch_bounds__(256, 1) void gemm_as_paths_kernel(GemmArgs p, int groups_n, int tpw) {
+__global__ __launch_bounds__(512, 1) void gemm_as_paths_kernel(GemmArgs p, int groups_n, int tpw) {
     constexpr int KG = KGP * NP, K = 128 * KG, LDK = K + 8;
     static_assert(K <= 1024 && NP >= 2, "paths block");
     __shared__ __attribute__((aligned(16))) _Float16 As[AS_BM * LDK];
-    constexpr int FM = 2, FN = 2, TN = 64, NKB = 8 * KGP;  // k-blocks per path
+    // 8 waves, each 64 rows x 32 columns of the 64 x 256 tile: two waves a
+    // SIMD, so one's VALU work and waits overlap the other's MFMAs
+    constexpr int NW = 8, NT = 64 * NW, FM = 2, FN = 1, TN = 32, NKB = 8 * KGP;  // NKB: k-blocks per path
     const int tid = threadIdx.x, lane = tid & 63;
     const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = p.N;
@@ -1203,13 +1206,13 @@ __global__ __launch_bounds__(256, 1) void gemm_as_paths_kernel(GemmArgs p, int g
 
     // bitmap words of path q for this lane's two plane rows of tile t: KGP
     // 16-byte groups per row, path q at Bbits + q * b_pstride words
-    u32x4_t w[2][2][KGP];
+    u32x4_t w[2][FN][KGP];
     const __amdgpu_buffer_rsrc_t rB =
         make_rsrc(p.Bbits, (uint64_t)(NP - 1) * p.b_pstride * 4 + (uint64_t)N * KGP * 16);
 #define ASP_WLOAD(buf, t_, q_)                                                             \
     do {                                                                                   \
-        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                    \
-            const uint32_t bo_ = (uint32_t)(((t_) * AS_BN + wn * 64 + j * 32 + (lane & 31)) * KGP * 16); \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                   \
+            const uint32_t bo_ = (uint32_t)(((t_) * AS_BN + wn * TN + j * 32 + (lane & 31)) * KGP * 16); \
             _Pragma("unroll") for (int g = 0; g < KGP; ++g) w[buf][j][g] =                 \
                 load_u32x4(rB, bo_, (uint32_t)((q_) * p.b_pstride * 4 + g * 16));          \
         }                                                                                  \
@@ -1224,14 +1227,14 @@ __global__ __launch_bounds__(256, 1) void gemm_as_paths_kernel(GemmArgs p, int g
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)M * p.lda * 4);
         const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.colscale, (uint64_t)K * 4);
         constexpr int cpr = K / 4, nch = AS_BM * cpr;
-        constexpr int UNR = 16;
-        constexpr bool onecol = 256 % cpr == 0;
+        constexpr int UNR = 8;
+        constexpr bool onecol = NT % cpr == 0;
         const f32x4_t c1 = onecol ? load_f32x4(rC, (uint32_t)(16 * (tid % cpr)), 0u) * p.ascale : f32x4_t{};
-        for (int i0 = 0; i0 < nch; i0 += 256 * UNR) {
+        for (int i0 = 0; i0 < nch; i0 += NT * UNR) {
             f32x4_t v[UNR], c[onecol ? 1 : UNR];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int i = i0 + u * 256 + tid;
+                const int i = i0 + u * NT + tid;
                 const int ic = i < nch ? i : nch - 1;
                 const int row = ic / cpr, c4 = ic - row * cpr;
                 int64_t gm = m0 + row;
@@ -1241,7 +1244,7 @@ __global__ __launch_bounds__(256, 1) void gemm_as_paths_kernel(GemmArgs p, int g
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int i = i0 + u * 256 + tid;
+                const int i = i0 + u * NT + tid;
                 if (i < nch) {
                     const int row = i / cpr, c4 = i - row * cpr;
                     const f32x4_t cs = onecol ? c1 : c[onecol ? 0 : u] * p.ascale;
@@ -1268,28 +1271,35 @@ __global__ __launch_bounds__(256, 1) void gemm_as_paths_kernel(GemmArgs p, int g
     const int64_t rl = m0 + 4 * (lane >> 5);
     const bool full = m0 + AS_BM <= M;
 
+    // the x of tile t_ (the dot operand of every path); a tile's is loaded
+    // while the previous tile's last path runs, ahead of that tile's stores
+    // (loads and stores share one counter, in order)
+#define ASP_UOFF(i, v, j) ((uint32_t)((8 * ((v) >> 2) + ((v) & 3)) * Ni + (j) * 32) * 4u)
+#define ASP_XLOAD(dst, t_)                                                                 \
+    do {                                                                                   \
+        int Nx_ = N;                                                                       \
+        asm volatile("" : "+s"(Nx_));                                                      \
+        const uint32_t lx_ = (uint32_t)((rl * Nx_ + (t_) * AS_BN + wn * TN + (lane & 31)) * 4); \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                   \
+            int Ni = Nx_;                                                                  \
+            asm volatile("" : "+s"(Ni));                                                   \
+            const uint32_t lo_ = lx_ + (uint32_t)(i * 32 * Ni * 4);                        \
+            _Pragma("unroll") for (int v = 0; v < 16; ++v) {                               \
+                const bool in_ = full || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M;         \
+                _Pragma("unroll") for (int j = 0; j < FN; ++j)                             \
+                    dst[i][j][v] = in_ ? load_f32_nt(rD, lo_, ASP_UOFF(i, v, j)) : 0.0f;   \
+            }                                                                              \
+        }                                                                                  \
+    } while (0)
+    float oth[FM][FN][16], othn[FM][FN][16];
+    ASP_XLOAD(oth, t0);
+
     for (int tt = 0; tt < tpw; ++tt) {
         const int t = t0 + tt;
         int Nl = N;
         asm volatile("" : "+s"(Nl));
         const int cb = t * AS_BN + wn * TN + (lane & 31);
         const uint32_t loff = (uint32_t)((rl * Nl + cb) * 4);
-#define ASP_UOFF(i, v, j) ((uint32_t)((8 * ((v) >> 2) + ((v) & 3)) * Ni + (j) * 32) * 4u)
-        // the tile's x (the dot operand of every path), loaded before the
-        // first path's MFMAs
-        float oth[FM][FN][16];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            int Ni = Nl;
-            asm volatile("" : "+s"(Ni));
-            const uint32_t lo_ = loff + (uint32_t)(i * 32 * Ni * 4);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const bool in_ = full || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M;
-#pragma unroll
-                for (int j = 0; j < FN; ++j) oth[i][j][v] = in_ ? load_f32_nt(rD, lo_, ASP_UOFF(i, v, j)) : 0.0f;
-            }
-        }
         f32x16_t ysum[FM][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -1304,10 +1314,11 @@ __global__ __launch_bounds__(256, 1) void gemm_as_paths_kernel(GemmArgs p, int g
                 ASP_WLOAD((q + 1) & 1, t, q + 1);
             } else if (tt + 1 < tpw) {
                 ASP_WLOAD((q + 1) & 1, t + 1, 0);
+                ASP_XLOAD(othn, t + 1);
             }
-            float c2[FN];
+            float c2[FN];  // g_p, times the output scale (the fragments hold -S)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) c2[j] = p.out2col[(int64_t)q * p.o2_pstride + cb + j * 32];
+            for (int j = 0; j < FN; ++j) c2[j] = p.out2col[(int64_t)q * p.o2_pstride + cb + j * 32] * osc;
             f32x16_t acc[FM][FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -1354,20 +1365,27 @@ __global__ __launch_bounds__(256, 1) void gemm_as_paths_kernel(GemmArgs p, int g
                 for (int v = 0; v < 16; ++v)
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        const float val = acc[i][j][v] * osc;
-                        ds[j] += val * oth[i][j][v];
-                        ysum[i][j][v] += val * c2[j];
+                        ds[j] += acc[i][j][v] * oth[i][j][v];
+                        ysum[i][j][v] += acc[i][j][v] * c2[j];
                     }
             // lanes l and l+32 hold other rows of the same column
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const float sum = ds[j] + __shfl_xor(ds[j], 32);
+                const float sum = (ds[j] + __shfl_xor(ds[j], 32)) * osc;
                 if (lane < 32) p.dot_partial[(int64_t)q * p.dot_pstride + (int64_t)mt * N + cb + j * 32] = sum;
             }
         }
+        if (tt + 1 < tpw) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) oth[i][j][v] = othn[i][j][v];
+        }
         if (NP & 1) {  // the next tile's first words arrived in buffer 1
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int g = 0; g < KGP; ++g) w[0][j][g] = w[1][j][g];
         }
@@ -1391,8 +1409,9 @@ __global__ __launch_bounds__(256, 1) void gemm_as_paths_kernel(GemmArgs p, int g
                     for (int j = 0; j < FN; ++j) store_f32_nt(rO2, lo_, ASP_UOFF(i, v, j), old[j][v] + ysum[i][j][v]);
                 }
         }
-#undef ASP_UOFF
     }
+#undef ASP_XLOAD
+#undef ASP_UOFF
 #undef ASP_WLOAD
 }
 
@@ -1405,7 +1424,7 @@ static hipError_t launch_gemm_as_paths_t(int id, const GemmArgs &a, hipStream_t 
     while (tpw * 2 <= 8 && ntiles % (tpw * 2) == 0 && mtiles * (ntiles / (tpw * 2)) >= 256) tpw *= 2;
     const int64_t gn = ntiles / tpw;
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_as_paths_kernel<KGP, NP>), dim3((unsigned)(mtiles * gn)), dim3(256), 0, s, a, (int)gn,
+    hipLaunchKernelGGL((gemm_as_paths_kernel<KGP, NP>), dim3((unsigned)(mtiles * gn)), dim3(512), 0, s, a, (int)gn,
                        tpw);
     hipError_t e = hipGetLastError();
     prof_end(s);
