@@ -20,8 +20,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
-// f16 bit patterns of +1 and -1.
-constexpr uint32_t F16_ONE = 0x3C00u;
+// f16 bit pattern of -1 (+1 is the same with the sign bit clear).
 constexpr uint32_t F16_MINUS_ONE = 0xBC00u;
 
 __device__ __forceinline__ uint32_t sign_pair(uint32_t b0, uint32_t b1) {
@@ -621,7 +620,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         BLR_AFRAG(fa, 0);
         BLR_BFRAG(fb, bq, 0, 0);
     }
-    int b0 = 0, b1 = 1, b2 = 2;  // LDS buffers of steps kt, kt+1 and kt+2
+    int b1 = 1, b2 = 2;  // LDS buffers of steps kt+1 and kt+2
 
 #define BLR_UOFF(i, v, j) ((uint32_t)(((i) * 32 + 8 * ((v) >> 2) + ((v) & 3)) * N + (j) * 32) * 4u)
     // MP: at the end of path q's ranks the product so far is scaled by the
@@ -768,7 +767,6 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                 // keep later steps' work out of this one: hoisted above the
                 // barrier it would wait for loads issued just before
                 __builtin_amdgcn_sched_barrier(0);
-                b0 = b1;
                 b1 = b2;
                 b2 = b2 == NS - 1 ? 0 : b2 + 1;
                 if (MP && ((kt + 1) * BK) % PKr == 0) BLR_FLUSH((kt + 1) * BK / PKr - 1);
@@ -1704,7 +1702,6 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
     // 8-byte writes at two passes and the fragments' 16-byte reads
     // conflict-free on gfx950 (measured)
     const int wofs = 4 * cq * TN2_LDK + 8 * ((tq >> 1) ^ (cq & 3)) + 4 * (tq & 1);
-    constexpr int BUFH = TN2_T * TN2_LDK;
     f32x4_t ra[TN2_TP][4], rb[TN2_TP][4];
     // Buffer loads: a token row at or past T lies past the buffer's range
     // and reads as zero (only the last range has a partial step; the others
