@@ -887,11 +887,11 @@ static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Short-K contraction with the activation block held in LDS (the kinds with
-// K = r: F2, B2). A workgroup of 4 waves loads the bitmap words of all its
+// K = r: F2, B2). A workgroup of 4 or 8 waves loads the bitmap words of its
 // tiles into registers, stages its 64 x K activation rows once (scaled and
 // rounded to f16, as in gemm_kernel), then walks a run of TPW consecutive
 // 64 x 256 output tiles with no further barrier and no load before its
-// epilogue: per tile each wave (64 rows x 64 columns) reads A fragments
+// epilogue: per tile each wave (64 rows x 64 or 32 columns) reads A fragments
 // from LDS, decodes B fragments from its words, and stores its block from
 // the accumulators, so one tile's stores drain while the next tile's MFMAs
 // run (a load issued after the stores would have to wait for them: vector
@@ -904,13 +904,16 @@ constexpr int AS_BM = 64, AS_BN = 256, AS_KMAX = 512;  // LDS: 64 x (K + 8) halv
 // and out2 (+)= sum over paths of out2col_q . product_q: path q's column scale
 // (rounded to f16) is folded into its decoded signs, so one sweep over K
 // forms the sum (no column partials in this mode).
-template <int KG, int TPW, bool OUT, bool OUT2, bool DOT, int PR = 0>
-__global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_n) {
+template <int KG, int TPW, bool OUT, bool OUT2, bool DOT, int PR = 0, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV, NWV / 2) void gemm_as_kernel(GemmArgs p, int groups_n) {
     constexpr int K = 128 * KG, LDK = K + 8;
     static_assert(PR == 0 || (OUT2 && !OUT && !DOT && KG % PR == 0), "paths folded along K");
     constexpr int NP = PR ? KG / PR : 1;  // paths
     __shared__ __attribute__((aligned(16))) _Float16 As[AS_BM * LDK];
-    constexpr int FM = 2, FN = 2, TN = 64;
+    // NWV waves, each 64 rows x 256 / NWV columns of a tile: 4 (64 x 64,
+    // two workgroups of 4 waves per CU) or 8 (64 x 32: four waves a SIMD,
+    // in at most 128 registers)
+    constexpr int NTH = 64 * NWV, TN = AS_BN / NWV, FM = 2, FN = TN / 32;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = p.N;
@@ -925,13 +928,13 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
     // groups per row; tile 0's first (they arrive while the block is
     // staged), each later tile's at the start of the one before
     constexpr int KW = PR ? PR * 4 : K / 32;  // bitmap words per plane row (of a path)
-    u32x4_t wall[TPW][2][KG];
+    u32x4_t wall[TPW][FN][KG];
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.Bbits, PR ? (uint64_t)(NP - 1) * p.b_pstride * 4 + (uint64_t)N * KW * 4
                                                             : (uint64_t)N * K / 8);
 #define AS_WLOAD(tt)                                                                       \
     do {                                                                                   \
-        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                    \
-            const uint32_t bo_ = (uint32_t)(((t0 + (tt)) * AS_BN + wn * 64 + j * 32 + (lane & 31)) * KW * 4); \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                   \
+            const uint32_t bo_ = (uint32_t)(((t0 + (tt)) * AS_BN + wn * TN + j * 32 + (lane & 31)) * KW * 4); \
             _Pragma("unroll") for (int g = 0; g < KG; ++g) wall[tt][j][g] = load_u32x4(rB, bo_, \
                 PR ? (uint32_t)((g / (PR ? PR : 1)) * p.b_pstride * 4 + (g % (PR ? PR : 1)) * 16) : (uint32_t)g * 16); \
         }                                                                                  \
@@ -964,33 +967,33 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)M * p.lda * 4);
         const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.colscale, (uint64_t)K * 4);
         constexpr int cpr = K / 4, nch = AS_BM * cpr;  // chunks per row, in the block
-        constexpr int UNR = nch / 256 < 32 ? nch / 256 : 32;
-        constexpr bool onecol = 256 % cpr == 0;
+        constexpr int UNR = nch / NTH < 32 ? nch / NTH : 32;
+        constexpr bool onecol = NTH % cpr == 0;
         const f32x4_t c1 = onecol ? load_f32x4(rC, (uint32_t)(16 * (tid % cpr)), 0u) : f32x4_t{};
         if (onecol && m0 + AS_BM <= M) {
             // full block: thread tid takes rows tid / cpr + u * (256 / cpr) of
             // column group tid % cpr; the row step is a uniform offset, so
             // every load is issued before the first is waited for
-            constexpr int rstep = 256 / (onecol ? cpr : 256);
+            constexpr int rstep = NTH / (onecol ? cpr : NTH);
             const int r0 = tid / cpr, c4 = tid % cpr;
             const uint32_t vb = (uint32_t)(((m0 + r0) * p.lda + 4 * c4) * 4);
-            f32x4_t v[nch / 256];
+            f32x4_t v[nch / NTH];
 #pragma unroll
-            for (int u = 0; u < nch / 256; ++u) v[u] = load_f32x4(rA, vb, (uint32_t)(u * rstep * p.lda * 4));
+            for (int u = 0; u < nch / NTH; ++u) v[u] = load_f32x4(rA, vb, (uint32_t)(u * rstep * p.lda * 4));
             const f32x4_t cs = c1 * p.ascale;
 #pragma unroll
-            for (int u = 0; u < nch / 256; ++u) {
+            for (int u = 0; u < nch / NTH; ++u) {
                 uint2 h;
                 h.x = f16x2_scaled(v[u].x, cs.x, v[u].y, cs.y);
                 h.y = f16x2_scaled(v[u].z, cs.z, v[u].w, cs.w);
                 *reinterpret_cast<uint2 *>(As + (r0 + u * rstep) * LDK + 4 * c4) = h;
             }
         } else
-        for (int i0 = 0; i0 < nch; i0 += 256 * UNR) {
+        for (int i0 = 0; i0 < nch; i0 += NTH * UNR) {
             f32x4_t v[UNR], c[onecol ? 1 : UNR];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int i = i0 + u * 256 + tid;
+                const int i = i0 + u * NTH + tid;
                 const int ic = i < nch ? i : nch - 1;
                 const int row = ic / cpr, c4 = ic - row * cpr;
                 int64_t gm = m0 + row;
@@ -1000,7 +1003,7 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int i = i0 + u * 256 + tid;
+                const int i = i0 + u * NTH + tid;
                 if (i < nch) {
                     const int row = i / cpr, c4 = i - row * cpr;
                     const f32x4_t cs = (onecol ? c1 : c[onecol ? 0 : u]) * p.ascale;
@@ -1148,12 +1151,12 @@ __global__ __launch_bounds__(256, 2) void gemm_as_kernel(GemmArgs p, int groups_
 #undef AS_WLOAD
 }
 
-template <int KG, int TPW, bool OUT, bool OUT2, bool DOT, int PR = 0>
+template <int KG, int TPW, bool OUT, bool OUT2, bool DOT, int PR = 0, int NWV = 4>
 static hipError_t launch_gemm_as_tt(int id, const GemmArgs &a, hipStream_t s) {
     const int64_t mtiles = (a.M + AS_BM - 1) / AS_BM;
     const int64_t gn = a.N / AS_BN / TPW;
     prof_begin(id, s);
-    hipLaunchKernelGGL((gemm_as_kernel<KG, TPW, OUT, OUT2, DOT, PR>), dim3((unsigned)(mtiles * gn)), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_as_kernel<KG, TPW, OUT, OUT2, DOT, PR, NWV>), dim3((unsigned)(mtiles * gn)), dim3(64 * NWV), 0, s,
                        a, (int)gn);
     hipError_t e = hipGetLastError();
     prof_end(s);
@@ -1167,9 +1170,11 @@ static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
     const int ntiles = a.N / AS_BN;
     // the longest run of tiles (its words fit in registers: TPW * KG <= 16)
     // that still gives about two workgroups per CU; the runs of one M tile
-    // land on one XCD
+    // land on one XCD. Without the dot operand a run of 4 takes 8 waves of
+    // 64 x 32 (four a SIMD): 14% faster than 4 waves of 64 x 64 for F2 at
+    // M = 8192, d = 4096, r = 512; with it they would spill.
     if (KG <= 4 && ntiles % 4 == 0 && mtiles * (ntiles / 4) >= 512)
-        return launch_gemm_as_tt<KG, 4, OUT, OUT2, DOT, PR>(id, a, s);
+        return launch_gemm_as_tt<KG, 4, OUT, OUT2, DOT, PR, DOT ? 4 : 8>(id, a, s);
     if (ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 512) return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT, PR>(id, a, s);
     return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT, PR>(id, a, s);
 }

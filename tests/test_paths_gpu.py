@@ -107,6 +107,29 @@ def test_paths_accumulate_rules(dev, M, d_in, d_out, r, P):
 
 
 @pytest.mark.gpu
+def test_paths_full_size_sampled(dev):
+    """Two paths of 256 ranks at M=8192, d=4096, the launches the two-path
+    benchmark line times (F2 in runs of four tiles on 8 waves with the paths'
+    h folded in, B2 on the multi-path held-activation kernel in runs of eight
+    tiles): with dy zero outside 48 sampled tokens, y, a and dx on the sample
+    and every path's dh, dl, dg against the oracle run on the sample alone."""
+    M, d_in, d_out, r, P = 8192, 4096, 4096, 256, 2
+    check_shapes_fit(M, d_in, d_out, P * r)
+    d = synth.custom_paths(M, d_in, d_out, r, P, seed=8505, dy_sigma=1e-6)
+    R = np.random.default_rng(M)
+    S = np.array(sorted(set(R.choice(M, size=45, replace=False).tolist()) | {0, M - 1, M - 65}))
+    run = dict(d)
+    run["dy"] = np.zeros_like(d["dy"])
+    run["dy"][S] = d["dy"][S]
+    say(f"paths full size M={M} d={d_in} r={r} P={P}, {len(S)} sampled tokens")
+    got = run_paths(run, float(d["gscale"]), dev)
+    got = {k: (v[S] if k in ("y", "a", "dx") else v) for k, v in got.items()}
+    sub = {k: d[k] for k in ("bits_u", "bits_v", "h", "l", "g")}
+    sub["x"], sub["dy"] = d["x"][S], d["dy"][S]
+    assert_close(got, want(sub))
+
+
+@pytest.mark.gpu
 def test_one_path_equals_the_plain_layer(dev):
     """paths = 1 takes the plain layer's launches: bit-identical outputs."""
     import torch
