@@ -1175,7 +1175,10 @@ static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
     // M = 8192, d = 4096, r = 512; with it they would spill.
     if (KG <= 4 && ntiles % 4 == 0 && mtiles * (ntiles / 4) >= 512)
         return launch_gemm_as_tt<KG, 4, OUT, OUT2, DOT, PR, DOT ? 4 : 8>(id, a, s);
-    if (ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 512) return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT, PR>(id, a, s);
+    // (a run of 2 with the dot operand spills: at M = 2048..8192, d = 4096,
+    // r = 512 it took 1.4-1.55x a run of 1 or 4, so that kind goes to runs of 1)
+    if (!DOT && ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 512)
+        return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT, PR>(id, a, s);
     return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT, PR>(id, a, s);
 }
 
