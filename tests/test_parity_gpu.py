@@ -302,3 +302,35 @@ def test_full_size_sampled_and_properties(dev, name):
         err = abs(float(terms.sum()) - L) / rss
         say(f"Euler identity {name_}: sum={float(terms.sum()):.6e} L={L:.6e} normalised error {err:.2e}")
         assert err <= TOL, name_
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [2048, 4096])
+def test_mid_size_sampled(dev, M):
+    """d = 4096, r = 512 at fewer tokens than the benchmark: the held-activation
+    launches take their shorter runs here (F2 runs of two tiles at M = 4096 and
+    of one at 2048, B2 runs of one tile), which the full sizes do not reach.
+    dy is zero outside 48
+    sampled tokens; y, a and dx on the sample and dh, dl, dg against the oracle
+    run on the sample alone."""
+    import torch
+    d_in = d_out = 4096
+    r = 512
+    check_shapes_fit(M, d_in, d_out, r)
+    d = synth.custom(M, d_in, d_out, r, seed=9100 + M, dy_sigma=1e-6)
+    S = sample_tokens(M)
+    t = to_dev(d, dev)
+    idx = torch.from_numpy(S).to(dev)
+    dy_s = torch.zeros_like(t["dy"])
+    dy_s[idx] = t["dy"][idx]
+    say(f"mid size M={M}: forward and backward with sampled dy")
+    y, ta, tc = blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"])
+    dh, dl, dg, dx = blr.blr_backward(t["x"], dy_s, t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
+                                      float(d["gscale"]))
+    torch.cuda.synchronize()
+    sub = {k: d[k] for k in ("bits_u", "bits_v", "h", "l", "g")}
+    sub["x"], sub["dy"] = d["x"][S], d["dy"][S]
+    want = run_oracle(sub)
+    got = {"y": host(y[idx]), "a": host(ta[idx]), "dh": host(dh), "dl": host(dl), "dg": host(dg),
+           "dx": host(dx[idx])}
+    assert_close(got, want)
