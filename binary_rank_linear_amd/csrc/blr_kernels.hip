@@ -1170,16 +1170,17 @@ static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
     const int ntiles = a.N / AS_BN;
     // the longest run of tiles (its words fit in registers: TPW * KG <= 16)
     // that still gives about two workgroups per CU; the runs of one M tile
-    // land on one XCD. Without the dot operand a run of 4 takes 8 waves of
-    // 64 x 32 (four a SIMD): 14% faster than 4 waves of 64 x 64 for F2 at
-    // M = 8192, d = 4096, r = 512; with it they would spill.
+    // land on one XCD. Without the dot operand every run takes 8 waves of
+    // 64 x 32 (four a SIMD): 5-14% faster than 4 waves of 64 x 64 for F2 at
+    // M = 2048..8192, d = 4096, r = 512; with it they would spill.
     if (KG <= 4 && ntiles % 4 == 0 && mtiles * (ntiles / 4) >= 512)
         return launch_gemm_as_tt<KG, 4, OUT, OUT2, DOT, PR, DOT ? 4 : 8>(id, a, s);
     // (a run of 2 with the dot operand spills: at M = 2048..8192, d = 4096,
     // r = 512 it took 1.4-1.55x a run of 1 or 4, so that kind goes to runs of 1)
-    if (!DOT && ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 512)
-        return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT, PR>(id, a, s);
-    return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT, PR>(id, a, s);
+    if constexpr (!DOT) {
+        if (ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 512) return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT, PR, 8>(id, a, s);
+    }
+    return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT, PR, DOT ? 4 : 8>(id, a, s);
 }
 
 // B2 of a layer of NP paths on the held activation block (K = NP paths of
