@@ -62,6 +62,7 @@ struct Layout {
     size_t bits_t;  // transposed bitmaps [P][r][max(d_in, d_out)/32] (u32)
     size_t db;      // f32 [M][P r]
     size_t part_h, part_l, part_g;
+    size_t part_s;  // sign gradients: partials of token ranges 1.. (f32)
     size_t total;
 };
 
@@ -85,6 +86,15 @@ Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P = 1) 
     off += up((size_t)(ceil_div(M, PART_ROWS_MIN) * P * r) * 4);
     L.part_g = off;
     off += up((size_t)(P * ceil_div(M, GEMM_BM_MIN) * d_in) * 4);
+    // the sign gradients' token ranges past the first (256 x 256 tiles only):
+    // (splits - 1) copies of G_U and G_V, under 64 MB whatever the shape
+    // (splits * tiles stays near 256)
+    L.part_s = off;
+    if (d_in % 256 == 0 && d_out % 256 == 0 && r % 256 == 0) {
+        const int64_t tiles = P * ((d_out / 256) * (r / 256) + (d_in / 256) * (r / 256));
+        const int64_t splits = sign_splits(tiles, M);
+        off += up((size_t)((splits - 1) * P * (d_out + d_in) * r) * 4);
+    }
     L.total = off;
     return L;
 }
@@ -417,11 +427,12 @@ static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int6
         TnJobs tj = {};
         tj.T = M;
         tj.count = 0;
+        tj.part = (float *)(ws + L.part_s);
         for (int64_t q = 0; q < P; ++q) {
             tj.job[tj.count++] = {dy, h + q * d_out, gscale, tape_a + q * r, l + q * r, 1.0f, (int)d_out, (int)r, inv,
-                                  grad_u + q * d_out * r, accumulate_signs ? 1 : 0, 0, d_out, Pr};
+                                  grad_u + q * d_out * r, accumulate_signs ? 1 : 0, 0, d_out, Pr, 0};
             tj.job[tj.count++] = {x, g + q * d_in, 1.0f, db + q * r, l + q * r, gscale, (int)d_in, (int)r, inv,
-                                  grad_v + q * d_in * r, accumulate_signs ? 1 : 0, 0, d_in, Pr};
+                                  grad_v + q * d_in * r, accumulate_signs ? 1 : 0, 0, d_in, Pr, 0};
         }
         BLR_TRY(launch_gemm_tn(tj, s));
     }

@@ -33,6 +33,7 @@ enum KernelId {
     K_GEMM_SIGNS, // sign gradients G_U, G_V (contractions over tokens)
     K_SUMSQ,      // sum-of-squares partials (finite check)
     K_GEMM_PLANE, // dense frozen f16 linear
+    K_SIGNS_REDUCE, // sign gradients: the token ranges' partials summed in order
     K_COUNT
 };
 const char *kernel_name(int id);
@@ -138,12 +139,22 @@ struct TnJob {
     int acc;
     int tiles_before;  // filled by the launcher
     int64_t lda, ldb;  // row strides of A and B (elements)
+    int64_t elems_before;  // filled by the launcher: sum of Mo * No of the jobs before
 };
 struct TnJobs {
     TnJob job[2 * MAX_PATHS];
     int count;
     int64_t T;
+    // Partial sums of token ranges 1 .. splits-1 (range 0 writes out itself):
+    // part[(s - 1) * part_stride + elems_before + m * No + n], with
+    // part_stride = sum over jobs of Mo * No. Needed when sign_splits() > 1.
+    float *part;
 };
+// Token ranges of the sign-gradient contraction on its 256 x 256 tiles:
+// enough ranges (each at least 512 tokens) to give about 256 workgroups over
+// `tiles256` output tiles, 1 when the tiles alone fill the GPU. Only shapes
+// whose output sizes are all multiples of 256 take those tiles (and ranges).
+int sign_splits(int64_t tiles256, int64_t T);
 
 // Launchers: enqueue on `s`, return the launch error (hipSuccess if none).
 hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s);

@@ -1660,8 +1660,10 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
 
 // The same contractions on 256x256 tiles, the tokens split into `splits`
 // ranges of tps tokens (a multiple of 32) so that the few large tiles still
-// fill the GPU; each range's partial sums are added to `out` atomically
-// (zeroed first unless the job accumulates). Per output element and token
+// fill the GPU. Range 0 writes (or adds to) `out`; every later range stores
+// its partial sums in the workspace, and sign_reduce_kernel then adds them
+// to `out` in range order, so the result does not depend on which range
+// finishes first (no atomics: reruns give identical bits). Per output element and token
 // this reads 8 bytes of activations for 256 + 256 products, half the bytes
 // per product of the 128x128 tiling. Blocks: job, then range, then tile, so
 // the tiles of one (job, range) run on one XCD and share their B rows and
@@ -1669,7 +1671,7 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
 // step of 32 tokens each thread stages a 4-token x 4-column block of both
 // operands (rounded to f16, transposed into LDS), two register stages ahead.
 constexpr int TN2_T = 256, TN2_LDK = 32, TN2_TP = 2;
-__global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int splits, int64_t tps) {
+__global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int splits, int64_t tps, int64_t part_stride) {
     __shared__ __attribute__((aligned(16))) _Float16 As[2][TN2_T * TN2_LDK];
     __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TN2_T * TN2_LDK];
     const int G = gridDim.x;
@@ -1792,8 +1794,10 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
 #undef TN2_LOAD
 #undef TN2_STORE
     // out row m0 + wm*64 + i*32 + 8*(v/4) + 4*(lane/32) + v%4, column
-    // n0 + wn*128 + jj*32 + lane%32: one range stores (or accumulates), several add
-    float *const o0 = outp + (int64_t)(m0 + wm * 64 + 4 * (lane >> 5)) * No + n0 + wn * 128 + (lane & 31);
+    // n0 + wn*128 + jj*32 + lane%32: range 0 stores (or accumulates) into
+    // out, range sp > 0 stores into its slice of the partials
+    float *const o0 = (sp == 0 ? outp : jobs.part + (int64_t)(sp - 1) * part_stride + jb.elems_before) +
+                      (int64_t)(m0 + wm * 64 + 4 * (lane >> 5)) * No + n0 + wn * 128 + (lane & 31);
 #define TN2_EPI(OP)                                                                        \
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                          \
         _Pragma("unroll") for (int v = 0; v < 16; ++v)                                     \
@@ -1802,9 +1806,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
                 const float val = acc[i][jj][v] * osc;                                     \
                 OP;                                                                        \
             }
-    if (splits > 1) {
-        TN2_EPI(unsafeAtomicAdd(o, val))
-    } else if (accf) {
+    if (sp == 0 && accf) {
         TN2_EPI(*o += val)
     } else {
         TN2_EPI(*o = val)
@@ -1812,19 +1814,28 @@ __global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int split
 #undef TN2_EPI
 }
 
-// zeroes the outputs of the jobs that do not accumulate (blockIdx.y = job)
-__global__ __launch_bounds__(256) void zero_outputs_kernel(TnJobs jobs) {
-    const TnJob &jb = jobs.job[blockIdx.y];
-    if (jb.acc) return;
-    const int64_t n = (int64_t)jb.Mo * jb.No;
-    float *const p = jb.out;
-    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * 1024) {
-        if (i + 4 <= n) {
-            *reinterpret_cast<f32x4_t *>(p + i) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        } else {
-            for (int64_t k = i; k < n; ++k) p[k] = 0.0f;
-        }
+// out += partials of token ranges 1 .. splits-1, in range order, for every
+// job's output (float4 groups over the jobs' outputs back to back; every
+// Mo * No is a multiple of 4).
+__global__ __launch_bounds__(256) void sign_reduce_kernel(TnJobs jobs, int splits, int64_t part_stride) {
+    const int64_t n4 = part_stride / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        const int64_t e = 4 * i;
+        int j = 0;
+        while (j + 1 < jobs.count && e >= jobs.job[j + 1].elems_before) ++j;
+        f32x4_t *o = reinterpret_cast<f32x4_t *>(jobs.job[j].out + (e - jobs.job[j].elems_before));
+        f32x4_t v = *o;
+        for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const f32x4_t *>(jobs.part + (int64_t)(s - 1) * part_stride + e);
+        *o = v;
     }
+}
+
+int sign_splits(int64_t tiles256, int64_t T) {
+    if (tiles256 < 1 || T < 1) return 1;
+    const int64_t steps = (T + 31) / 32;
+    int64_t splits = (256 + tiles256 - 1) / tiles256;
+    if (splits > steps / 16) splits = steps / 16;
+    return splits < 1 ? 1 : (int)splits;
 }
 
 hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
@@ -1834,15 +1845,19 @@ hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
         if (jobs.job[j].Mo % TN_BM || jobs.job[j].No % TN_BN) return hipErrorInvalidValue;
         if (jobs.job[j].Mo % TN2_T || jobs.job[j].No % TN2_T) big = false;
     }
+    int64_t elems = 0;
+    for (int j = 0; j < jobs.count; ++j) {
+        jobs.job[j].elems_before = elems;
+        elems += (int64_t)jobs.job[j].Mo * jobs.job[j].No;
+    }
     if (big) {
         // tiles of all jobs, then as many token ranges (of at least 512
         // tokens) as bring the workgroups to about 256
         int tiles = 0;
         for (int j = 0; j < jobs.count; ++j) tiles += (jobs.job[j].Mo / TN2_T) * (jobs.job[j].No / TN2_T);
         const int64_t steps = (jobs.T + 31) / 32;
-        int splits = (256 + tiles - 1) / tiles;
-        if (splits > steps / 16) splits = (int)(steps / 16);
-        if (splits < 1) splits = 1;
+        const int splits = sign_splits(tiles, jobs.T);
+        if (splits > 1 && jobs.part == nullptr) return hipErrorInvalidValue;
         const int64_t tps = ((steps + splits - 1) / splits) * 32;
         int total = 0;
         for (int j = 0; j < jobs.count; ++j) {
@@ -1850,10 +1865,15 @@ hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
             total += (jobs.job[j].Mo / TN2_T) * (jobs.job[j].No / TN2_T) * splits;
         }
         prof_begin(K_GEMM_SIGNS, s);
-        if (splits > 1 && !jobs.job[0].acc)  // (every job accumulates, or none)
-            hipLaunchKernelGGL(zero_outputs_kernel, dim3(1024, (unsigned)jobs.count), dim3(256), 0, s, jobs);
-        hipLaunchKernelGGL(gemm_tn2_kernel, dim3((unsigned)total), dim3(512), 0, s, jobs, splits, tps);
+        hipLaunchKernelGGL(gemm_tn2_kernel, dim3((unsigned)total), dim3(512), 0, s, jobs, splits, tps, elems);
         hipError_t e = hipGetLastError();
+        prof_end(s);
+        if (e != hipSuccess || splits == 1) return e;
+        int64_t blocks = (elems / 4 + 255) / 256;
+        if (blocks > 2048) blocks = 2048;
+        prof_begin(K_SIGNS_REDUCE, s);
+        hipLaunchKernelGGL(sign_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, jobs, splits, elems);
+        e = hipGetLastError();
         prof_end(s);
         return e;
     }
@@ -2014,6 +2034,7 @@ const char *kernel_name(int id) {
         case K_GEMM_SIGNS: return "gemm_sign_grads";
         case K_SUMSQ: return "sumsq";
         case K_GEMM_PLANE: return "gemm_plane_linear";
+        case K_SIGNS_REDUCE: return "sign_grads_reduce";
     }
     return "?";
 }

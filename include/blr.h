@@ -68,8 +68,10 @@ const char *blr_status_string(int status);
  * otherwise (the page's `matrix_units` capability check). */
 int blr_device_supported(int hip_device);
 
-/* Bytes of device workspace blr_forward and blr_backward need for these
- * sizes (the same figure serves both). 0 for invalid sizes. */
+/* Bytes of device workspace blr_forward, blr_backward and
+ * blr_backward_signs need for these sizes (the same figure serves all
+ * three; it includes the token-range partials of the sign gradients, under
+ * 64 MB for any shape). 0 for invalid sizes. */
 size_t blr_workspace_bytes(int64_t M, int64_t d_in, int64_t d_out, int64_t r);
 
 /*
@@ -131,8 +133,11 @@ int blr_backward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float 
  * are contractions over the tokens of f16-staged operands with f32
  * accumulation: f16(dy.h.gscale) with f16(a.l), and f16(x.g) with
  * f16(db.l.gscale), each product divided by gscale. accumulate_signs = 0
- * overwrites grad_u / grad_v, 1 adds. Every other argument, rule and error
- * is blr_backward's; grad_u and grad_v must be non-NULL and 16-byte aligned.
+ * overwrites grad_u / grad_v, 1 adds. Where the tokens are split into ranges
+ * to fill the GPU, each range's partial sums are kept in the workspace and
+ * added in range order, so reruns give identical bits here too. Every other
+ * argument, rule and error is blr_backward's; grad_u and grad_v must be
+ * non-NULL and 16-byte aligned.
  */
 int blr_backward_signs(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const float *dy,
                        const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l, const float *g,

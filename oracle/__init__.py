@@ -6,8 +6,8 @@ with the HIP library and imports nothing from it.
 
 Source: the cortiq-engine page "src/gpu_wgpu/train_mm.rs" (0.8.21): module
 doc block (layer and equations), `expand` shader (bit convention),
-`blr_forward` / `blr_backward` (overwrite/accumulate rules), and the f64
-host reference of test `blr_layer_matches_host`.
+`blr_forward` / `blr_backward` (overwrite/accumulate rules); the acceptance
+measure `rel_frobenius` is the relative error of the page's layer test.
 
 Every function takes numpy arrays; floating inputs are promoted to f64
 exactly. Every function here is pinned by tests/test_oracle.py against

@@ -6,12 +6,15 @@
  * CPU-baseline leg do. It shares no code, header, table or helper with the
  * HIP library.
  *
- * Source: the cortiq-engine page "src/gpu_wgpu/train_mm.rs" (0.8.21), its
- * module doc block (the layer W^ = diag(h) S_U diag(l) S_V^T diag(g) and
- * the forward/backward equations), the `expand` shader (bit convention),
- * `blr_forward` / `blr_backward` (overwrite and accumulate rules), and the
- * f64 host reference inside test `blr_layer_matches_host`, which this file
- * follows step for step, one token at a time.
+ * Source: the cortiq-engine page "src/gpu_wgpu/train_mm.rs" (0.8.21): the
+ * module doc block (the layer W^ = diag(h) S_U diag(l) S_V^T diag(g) and its
+ * forward and backward equations), the `expand` shader (bit convention) and
+ * `blr_forward` / `blr_backward` (overwrite and accumulate rules).
+ *
+ * Loop order (this file's own): per token, the forward forms a, then c, then
+ * y from the equations; the backward forms db and dx' per token into
+ * per-token arrays, and the column sums dh, dl, dg run over the tokens in
+ * index order afterwards.
  *
  * Exact maths in f64; f32 staging and f16 rounding are NOT simulated (the
  * method reaches this result up to the rounding of its staged operands).

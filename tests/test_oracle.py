@@ -445,6 +445,47 @@ def test_sumsq_closed_forms_and_non_finite():
     assert np.isnan(oracle.sumsq(np.array([np.inf, -np.inf, np.nan])))
 
 
+# ------------------------------------------------ the acceptance measure --
+# rel = ||got - want||_F / max(||want||_F, 1e-15), the measure of test
+# `blr_layer_matches_host` on the page (its `rel` closure). Every GPU parity
+# verdict rests on it, so it is pinned by values that a dropped square root,
+# a dropped floor or a swapped argument would change.
+
+def test_rel_frobenius_closed_forms():
+    w = np.array([[3.0, -4.0], [12.0, 0.0]])  # ||w|| = 13
+    assert oracle.rel_frobenius(2 * w, w) == 1.0
+    assert oracle.rel_frobenius(w, w) == 0.0
+    assert oracle.rel_frobenius(np.zeros_like(w), w) == 1.0
+    # got = w (1 + eps) with eps a power of two: every difference is exact,
+    # so the measure is eps exactly (without the root it would be eps^2)
+    for eps in (2.0 ** -1, 2.0 ** -10, 2.0 ** -20):
+        assert oracle.rel_frobenius(w * (1 + eps), w) == eps
+    # ||e|| = 2.5 against ||want|| = 5: 0.5 (0.25 without the root)
+    assert oracle.rel_frobenius(np.array([4.5, 6.0]), np.array([3.0, 4.0])) == 0.5
+    # asymmetric: the norm of the second argument is the denominator
+    assert oracle.rel_frobenius(np.array([3.0, 4.0]), np.array([6.0, 8.0])) == 0.5
+    assert oracle.rel_frobenius(np.array([6.0, 8.0]), np.array([3.0, 4.0])) == 1.0
+    # f32 inputs are promoted exactly
+    assert oracle.rel_frobenius(np.float32([4.5, 6.0]), np.float32([3.0, 4.0])) == 0.5
+
+
+def test_rel_frobenius_floor_for_a_zero_reference():
+    """A zero reference divides by the floor 1e-15 (the page's
+    max(norm, 1e-15)), so a got of norm 5e-16 reads 0.5 and an exact zero 0."""
+    z = np.zeros(2)
+    assert oracle.rel_frobenius(z, z) == 0.0
+    assert abs(oracle.rel_frobenius(np.array([3e-16, 4e-16]), z) - 0.5) < 1e-12
+    assert abs(oracle.rel_frobenius(np.array([3e-13, 4e-13]), z) - 500.0) < 1e-9
+    # the floor only acts below it
+    assert abs(oracle.rel_frobenius(np.array([3e-15, 4e-15]), np.array([6e-15, 8e-15])) - 0.5) < 1e-12
+
+
+def test_rel_frobenius_non_finite_fails_the_bar():
+    w = np.array([1.0, 2.0])
+    assert not oracle.rel_frobenius(np.array([np.nan, 2.0]), w) <= 3e-3
+    assert not oracle.rel_frobenius(np.array([np.inf, 2.0]), w) <= 3e-3
+
+
 # ----------------------------------------------------------- plane_linear --
 
 def test_f16_decode_matches_numpy_float16():

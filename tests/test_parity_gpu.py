@@ -5,8 +5,11 @@ Bar (test `blr_layer_matches_host` on the cortiq-engine train_mm.rs page):
 relative Frobenius error <= 3e-3 for y, dx, dh, dl, dg (and the tapes a, c).
 
 Small shapes run the oracle on every token and span several 128-row tiles
-with ragged tails. The full workload sizes run the GPU on all tokens, in the
-same launch configuration the benchmark times, and check
+with ragged tails. The attention-projection layer, the MLP up and down
+layers and the mid sizes are compared with the oracle on every token and
+every output, with dense dy, in the launch configuration the benchmark
+times. The ragged 30000-token layer (about 40x the oracle work of the
+attention projection) runs the GPU on all tokens and checks
   * a sample of tokens against the oracle: per-token outputs (y, a, c, dx)
     depend only on that token, and with dy zero outside the sample the
     column sums dh, dl, dg reduce to the sampled tokens exactly;
@@ -120,17 +123,21 @@ def test_windows_workload_full_oracle(dev):
 
 
 @pytest.mark.gpu
-def test_accumulate_flags(dev):
+@pytest.mark.parametrize("M,d_in,d_out,r,keep_c", [
+    (200, 256, 384, 128, False),   # d_out not a multiple of 256: the generic F2 and B2
+    (200, 512, 512, 256, False),   # the held-activation F2 and B2 epilogues
+    (130, 256, 768, 512, True),    # held activation with the c tape, ragged tail
+])
+def test_accumulate_flags(dev, M, d_in, d_out, r, keep_c):
     """y += h.c and dx += g.dx' when asked; dh, dl, dg always accumulate."""
-    M, d_in, d_out, r = 200, 256, 384, 128
     d = synth.custom(M, d_in, d_out, r, seed=11, dy_sigma=1e-6)
     R = np.random.default_rng(4)
     y0 = R.standard_normal((M, d_out)).astype(np.float32)
     dx0 = R.standard_normal((M, d_in)).astype(np.float32) * np.float32(1e-5)
     g0 = tuple((R.standard_normal(n) * s).astype(np.float32) for n, s in ((d_out, 1e-4), (r, 1e-3), (d_in, 1e-4)))
     gs = float(d["gscale"])
-    say("accumulate y and dx, nonzero dh/dl/dg")
-    got = run_gpu(d, gs, dev, y0=y0, acc_y=True, grads0=g0, dx0=dx0, acc_dx=True)
+    say(f"accumulate y and dx, nonzero dh/dl/dg, M={M} d_in={d_in} d_out={d_out} r={r} keep_c={keep_c}")
+    got = run_gpu(d, gs, dev, y0=y0, acc_y=True, grads0=g0, dx0=dx0, acc_dx=True, keep_c=keep_c)
     want = run_oracle(d, y0=y0, acc_y=True, grads0=g0, dx0=dx0, acc_dx=True)
     assert_close(got, want)
 
@@ -245,8 +252,8 @@ def test_writes_exactly_m_rows(dev):
 
 # ------------------------------------------------------------ full sizes --
 
-FULL = ["attn_proj_8192x4096x4096_r512", "mlp_up_8192x4096x12288_r1024", "mlp_down_8192x12288x4096_r1024",
-        "ragged_30000x5120x17408_r2048"]
+FULL_ORACLE = ["attn_proj_8192x4096x4096_r512", "mlp_up_8192x4096x12288_r1024", "mlp_down_8192x12288x4096_r1024"]
+RAGGED = "ragged_30000x5120x17408_r2048"
 
 
 def sample_tokens(M: int, n: int = 48) -> np.ndarray:
@@ -256,23 +263,61 @@ def sample_tokens(M: int, n: int = 48) -> np.ndarray:
     return np.array(sorted(s))
 
 
-@pytest.mark.gpu
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_and_properties(dev, name):
+def euler_identities(t, y, dh, dl, dg, dx):
+    """With dense dy, L = sum(dy.y) and, y being linear in each of h, l, g
+    and x, sum(h.dh) = sum(l.dl) = sum(g.dg) = sum(x.dx) = L."""
+    f64 = lambda v: v.double()
+    L = float((f64(t["dy"]) * f64(y)).sum())
     import torch
+    for name_, theta, grad in (("h", t["h"], dh), ("l", t["l"], dl), ("g", t["g"], dg), ("x", t["x"], dx)):
+        terms = f64(theta) * f64(grad)
+        rss = float(torch.sqrt((terms * terms).sum()))
+        err = abs(float(terms.sum()) - L) / rss
+        say(f"Euler identity {name_}: sum={float(terms.sum()):.6e} L={L:.6e} normalised error {err:.2e}")
+        assert err <= TOL, name_
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", FULL_ORACLE)
+def test_full_size_full_oracle(dev, name):
+    """Every token and every output against the oracle, with dense dy, in the
+    benchmark's launch configuration (no c tape: c recomputed in the
+    backward)."""
     w = synth.WORKLOADS[name]
+    check_shapes_fit(w.M, w.d_in, w.d_out, w.r)
+    d = synth.inputs(w)
+    t = to_dev(d, dev)
+    ws = blr.workspace(w.M, w.d_in, w.d_out, w.r, dev)
+    say(f"full size {name}: forward and backward on the GPU")
+    y, ta, tc = blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ws=ws)
+    assert tc is None
+    dh, dl, dg, dx = blr.blr_backward(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
+                                      w.gscale, ws=ws)
+    import torch
+    torch.cuda.synchronize()
+    got = {"y": host(y), "a": host(ta), "dh": host(dh), "dl": host(dl), "dg": host(dg), "dx": host(dx)}
+    euler_identities(t, y, dh, dl, dg, dx)
+    del y, ta, dh, dl, dg, dx, t
+    say(f"full size {name}: oracle on all {w.M} tokens")
+    assert_close(got, run_oracle(d))
+
+
+@pytest.mark.gpu
+def test_ragged_full_size_sampled_and_properties(dev):
+    import torch
+    w = synth.WORKLOADS[RAGGED]
     check_shapes_fit(w.M, w.d_in, w.d_out, w.r)
     d = synth.inputs(w)
     S = sample_tokens(w.M)
     t = to_dev(d, dev)
     ws = blr.workspace(w.M, w.d_in, w.d_out, w.r, dev)
-    say(f"full size {name}: forward")
+    say(f"full size {RAGGED}: forward")
     y, ta, tc = blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ws=ws)
     # (1) dy zero outside the sample: the column sums reduce to the sample
     dy_s = torch.zeros_like(t["dy"])
     idx = torch.from_numpy(S).to(dev)
     dy_s[idx] = t["dy"][idx]
-    say(f"full size {name}: backward with sampled dy")
+    say(f"full size {RAGGED}: backward with sampled dy")
     dh, dl, dg, dx = blr.blr_backward(t["x"], dy_s, t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
                                       w.gscale, ws=ws)
     torch.cuda.synchronize()
@@ -287,50 +332,34 @@ def test_full_size_sampled_and_properties(dev, name):
     mask[idx] = False
     assert int(torch.count_nonzero(dx[mask])) == 0, "dx must be exactly zero where dy is zero"
     # (2) dense dy: per-token dx on the sample, and the Euler identities
-    say(f"full size {name}: backward with dense dy")
+    say(f"full size {RAGGED}: backward with dense dy")
     dh, dl, dg, dx = blr.blr_backward(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
                                       w.gscale, ws=ws)
     torch.cuda.synchronize()
     # dx of a token depends on that token's dy alone; sub["dy"] is the dense dy on the sample
     want_dx = oracle.backward(sub["x"], sub["dy"], sub["bits_u"], sub["bits_v"], sub["h"], sub["l"], sub["g"])[3]
     assert oracle.rel_frobenius(host(dx[idx]), want_dx) <= TOL
-    f64 = lambda v: v.double()
-    L = float((f64(t["dy"]) * f64(y)).sum())
-    for name_, theta, grad in (("h", t["h"], dh), ("l", t["l"], dl), ("g", t["g"], dg), ("x", t["x"], dx)):
-        terms = f64(theta) * f64(grad)
-        rss = float(torch.sqrt((terms * terms).sum()))
-        err = abs(float(terms.sum()) - L) / rss
-        say(f"Euler identity {name_}: sum={float(terms.sum()):.6e} L={L:.6e} normalised error {err:.2e}")
-        assert err <= TOL, name_
+    euler_identities(t, y, dh, dl, dg, dx)
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("M", [2048, 4096])
-def test_mid_size_sampled(dev, M):
+@pytest.mark.parametrize("M", [2048, 4000, 4096])
+def test_mid_size_full_oracle(dev, M):
     """d = 4096, r = 512 at fewer tokens than the benchmark: the held-activation
-    launches take their shorter runs here (F2 runs of two tiles at M = 4096 and
-    of one at 2048, B2 runs of one tile), which the full sizes do not reach.
-    dy is zero outside 48
-    sampled tokens; y, a and dx on the sample and dh, dl, dg against the oracle
-    run on the sample alone."""
+    launches take their shorter runs here (F2 runs of two tiles at M = 4096
+    and 4000, the latter with a ragged last row tile, and of one at 2048; B2
+    runs of one tile), which the full sizes do not reach. Every token and
+    every output against the oracle, with dense dy."""
     import torch
     d_in = d_out = 4096
     r = 512
     check_shapes_fit(M, d_in, d_out, r)
     d = synth.custom(M, d_in, d_out, r, seed=9100 + M, dy_sigma=1e-6)
-    S = sample_tokens(M)
     t = to_dev(d, dev)
-    idx = torch.from_numpy(S).to(dev)
-    dy_s = torch.zeros_like(t["dy"])
-    dy_s[idx] = t["dy"][idx]
-    say(f"mid size M={M}: forward and backward with sampled dy")
+    say(f"mid size M={M}: forward and backward")
     y, ta, tc = blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"])
-    dh, dl, dg, dx = blr.blr_backward(t["x"], dy_s, t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
+    dh, dl, dg, dx = blr.blr_backward(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
                                       float(d["gscale"]))
     torch.cuda.synchronize()
-    sub = {k: d[k] for k in ("bits_u", "bits_v", "h", "l", "g")}
-    sub["x"], sub["dy"] = d["x"][S], d["dy"][S]
-    want = run_oracle(sub)
-    got = {"y": host(y[idx]), "a": host(ta[idx]), "dh": host(dh), "dl": host(dl), "dg": host(dg),
-           "dx": host(dx[idx])}
-    assert_close(got, want)
+    got = {"y": host(y), "a": host(ta), "dh": host(dh), "dl": host(dl), "dg": host(dg), "dx": host(dx)}
+    assert_close(got, run_oracle(d))

@@ -96,8 +96,11 @@ def test_paths_sign_grads(dev):
                                                (130, 512, 256, 512, 2)])
 def test_paths_accumulate_rules(dev, M, d_in, d_out, r, P):
     """y += sum_p h_p.c_p and dx += sum_p g_p.dx'_p when asked. Every shape
-    takes the held-activation B2 over the paths in turn; the first two the
-    held-activation F2 with the paths' h folded in, the third the generic F2."""
+    takes the held-activation B2 over the paths in turn (d_in a multiple of
+    256, P r <= 1024). The second takes the held-activation F2 with the
+    paths' h folded in; the first (d_out = 384, not a multiple of 256) and the
+    third (P r = 1024, past the held block) take the generic F2 with one
+    flush per path."""
     d = synth.custom_paths(M, d_in, d_out, r, P, seed=8202 + r, dy_sigma=1e-6)
     R = np.random.default_rng(5)
     y0 = R.standard_normal((M, d_out)).astype(np.float32)

@@ -79,8 +79,8 @@ def test_sign_grads_accumulate_and_c_tape(dev):
 @pytest.mark.gpu
 def test_sign_grads_accumulate_over_token_ranges(dev):
     # d and r multiples of 256 and 35 steps of 32 tokens: the 256x256 tiles
-    # with the tokens split in two ranges whose partial sums are added
-    # atomically, onto the caller's values (accumulate) and onto zeros
+    # with the tokens split in two ranges; the first writes (or adds to) the
+    # output, the second's partial sums are added after it, in range order
     M, d_in, d_out, r = 1100, 512, 256, 256
     d = synth.custom(M, d_in, d_out, r, seed=23, dy_sigma=1e-6)
     gs = float(d["gscale"])
@@ -113,6 +113,9 @@ def test_sign_grads_gscale_invariance_and_negative_control(dev):
 
 @pytest.mark.gpu
 def test_sign_grads_attention_projection_full_size(dev):
+    """The full attention-projection layer, where the tokens are split into
+    four ranges whose partials are summed in range order: against the oracle,
+    and bit-identical over two runs (the ranges finish in any order)."""
     w = synth.WORKLOADS[synth.HEADLINE]
     check_shapes_fit(w.M, w.d_in, w.d_out, w.r)
     d = synth.inputs(w)
@@ -121,3 +124,23 @@ def test_sign_grads_attention_projection_full_size(dev):
     GU, GV = oracle.sign_grads(d["x"], d["dy"], d["bits_u"], d["bits_v"], d["h"], d["l"], d["g"])
     assert oracle.rel_frobenius(gu, GU) < TOL
     assert oracle.rel_frobenius(gv, GV) < TOL
+    say(f"sign gradients at full size {w.name}: second run, bit for bit")
+    _, _, _, _, gu2, gv2 = run_signs(d, w.gscale, dev)
+    assert np.array_equal(gu, gu2) and np.array_equal(gv, gv2)
+
+
+@pytest.mark.gpu
+def test_sign_grads_reruns_are_bit_identical(dev):
+    """Token ranges at a mid size (two of them), accumulate and overwrite:
+    two runs give the same bits."""
+    M, d_in, d_out, r = 1100, 512, 256, 256
+    d = synth.custom(M, d_in, d_out, r, seed=31, dy_sigma=1e-6)
+    gs = float(d["gscale"])
+    g0 = np.random.default_rng(2).standard_normal((d_out, r)) * 1e-3
+    v0 = np.random.default_rng(3).standard_normal((d_in, r)) * 1e-3
+    for acc in (False, True):
+        say(f"sign gradients rerun identity, accumulate={acc}")
+        a = run_signs(d, gs, dev, gu0=g0, gv0=v0, acc=acc)
+        b = run_signs(d, gs, dev, gu0=g0, gv0=v0, acc=acc)
+        for k in range(6):
+            assert np.array_equal(a[k], b[k]), k
