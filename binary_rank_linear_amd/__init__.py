@@ -7,7 +7,7 @@ There is no fallback: if the library is missing or the device is not
 gfx950, the calls raise.
 
 The functions carry the C names: `blr_expand_signs`, `blr_forward`,
-`blr_backward`, `blr_backward_signs`, `blr_plane_linear`, `blr_sumsq`, `blr_workspace_bytes`,
+`blr_forward_noalloc`, `blr_backward`, `blr_backward_signs`, `blr_plane_linear`, `blr_sumsq`, `blr_workspace_bytes`,
 plus the profiling calls; `all_finite` and `next_gscale` are the host side
 of the finite check and the power-of-two loss scale.
 """
@@ -46,6 +46,8 @@ def load():
     lib.blr_expand_signs.restype = i32
     lib.blr_forward.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, i32, p, p, p, sz, p]
     lib.blr_forward.restype = i32
+    lib.blr_forward_noalloc.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, i32, p, p, p]
+    lib.blr_forward_noalloc.restype = i32
     lib.blr_backward.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, f32, p, p, p, p, i32, p, sz, p]
     lib.blr_backward.restype = i32
     lib.blr_backward_signs.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, f32, p, p, p, p, i32, p, p, i32,
@@ -176,6 +178,34 @@ def blr_forward(x, bits_u, bits_v, h, l, g, *, y=None, accumulate_y=False, tape_
     _check(load().blr_forward(M, d_in, d_out, r, _ptr(x), _ptr(bits_u), _ptr(bits_v), _ptr(h), _ptr(l), _ptr(g),
                               _ptr(y), int(bool(accumulate_y)), _ptr(tape_a), _ptr(tape_c), _ptr(ws), ws.numel(),
                               _stream(stream)), "blr_forward")
+    return y, tape_a, tape_c
+
+
+# bytes of the allocation-free forward's scratch (BLR_NOALLOC_SCRATCH_BYTES):
+# it serves sizes with r * d_in / 8 up to this
+NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def blr_forward_noalloc(x, bits_u, bits_v, h, l, g, y, tape_a, *, accumulate_y=False, tape_c=None, stream=None):
+    """blr_forward without a workspace and without allocating: every output
+    (y, tape_a, and tape_c if kept) is the caller's; the library's own
+    per-GPU scratch holds the transposed bitmap. Calls that overlap on one
+    GPU race. Returns (y, tape_a, tape_c)."""
+    import torch
+    f32 = (torch.float32,)
+    M, d_in = _need(x, "x", f32).shape
+    d_out, r = _need(h, "h", f32).shape[0], _need(l, "l", f32).shape[0]
+    _need(g, "g", f32, (d_in,))
+    W = (r + 31) // 32
+    _need(bits_u, "bits_u", _bits_dtypes(), (d_out, W))
+    _need(bits_v, "bits_v", _bits_dtypes(), (d_in, W))
+    _need(y, "y", f32, (M, d_out))
+    _need(tape_a, "tape_a", f32, (M, r))
+    if tape_c is not None:
+        _need(tape_c, "tape_c", f32, (M, d_out))
+    _check(load().blr_forward_noalloc(M, d_in, d_out, r, _ptr(x), _ptr(bits_u), _ptr(bits_v), _ptr(h), _ptr(l),
+                                      _ptr(g), _ptr(y), int(bool(accumulate_y)), _ptr(tape_a), _ptr(tape_c),
+                                      _stream(stream)), "blr_forward_noalloc")
     return y, tape_a, tape_c
 
 

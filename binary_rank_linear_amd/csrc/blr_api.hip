@@ -165,6 +165,7 @@ const char *blr_status_string(int status) {
         case BLR_ERR_DEVICE: return "the current device is not gfx950";
         case BLR_ERR_HIP: return "HIP runtime error";
         case BLR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case BLR_ERR_SCRATCH: return "sizes need more than the allocation-free forward's scratch (r * d_in / 8 bytes)";
     }
     return "unknown status";
 }
@@ -199,25 +200,27 @@ int blr_expand_signs(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl
 // h [P][d_out], l [P][r], g [P][d_in]; the a tape is [M][P r] (the paths'
 // ranks side by side). F1 runs once over the concatenated ranks; F2 runs
 // once with the paths along K (one flush per path) when P > 1.
-static int forward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P, const float *x,
-                        const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
-                        const float *g, float *y, int accumulate_y, float *tape_a, float *tape_c, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+// Arguments of the forward, workspace aside.
+static int forward_check(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P, const float *x,
+                         const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                         const float *g, const float *y, const float *tape_a, const float *tape_c) {
     if (!x || !bits_u || !bits_v || !h || !l || !g || !y || !tape_a) return BLR_ERR_NULL;
     if (!shape_ok(M, d_in, d_out, r, P)) return BLR_ERR_SHAPE;
     if (P > 1 && tape_c) return BLR_ERR_SHAPE;  // no c tape for several paths
-    const Layout L = layout(M, d_in, d_out, r, P);
-    if (workspace == nullptr || workspace_bytes < L.total) return BLR_ERR_WORKSPACE;
-    const void *f16a[] = {x, h, l, g, y, tape_a, tape_c ? tape_c : tape_a, workspace};
+    const void *f16a[] = {x, h, l, g, y, tape_a, tape_c ? tape_c : tape_a};
     for (const void *p : f16a)
         if (!aligned16(p)) return BLR_ERR_ALIGN;
     if (!aligned16(bits_u) || !aligned16(bits_v)) return BLR_ERR_ALIGN;
-    int st = current_device_ok();
-    if (st != BLR_OK) return st;
+    return BLR_OK;
+}
 
-    hipStream_t s = (hipStream_t)stream;
-    char *ws = (char *)workspace;
-    uint32_t *bits_vt = (uint32_t *)(ws + L.bits_t);  // S_V^T per path, [P][r][d_in/32]
+// The forward's launches, after validation. bits_vt: room for the
+// transposed S_V bitmaps, [P][r][d_in/32] u32 (16-byte aligned), the only
+// scratch the forward uses.
+static int forward_launch(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P, const float *x,
+                          const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                          const float *g, float *y, int accumulate_y, float *tape_a, float *tape_c,
+                          uint32_t *bits_vt, hipStream_t s) {
     BLR_TRY(launch_transpose_bits(bits_v, d_in, r, bits_vt, s, (int)P));
 
     GemmArgs f1 = {};
@@ -262,11 +265,68 @@ static int forward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64
     return BLR_OK;
 }
 
+static int forward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P, const float *x,
+                        const uint32_t *bits_u, const uint32_t *bits_v, const float *h, const float *l,
+                        const float *g, float *y, int accumulate_y, float *tape_a, float *tape_c, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    int st = forward_check(M, d_in, d_out, r, P, x, bits_u, bits_v, h, l, g, y, tape_a, tape_c);
+    if (st != BLR_OK) return st;
+    const Layout L = layout(M, d_in, d_out, r, P);
+    if (workspace == nullptr || workspace_bytes < L.total) return BLR_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return BLR_ERR_ALIGN;
+    st = current_device_ok();
+    if (st != BLR_OK) return st;
+    uint32_t *bits_vt = (uint32_t *)((char *)workspace + L.bits_t);  // S_V^T per path, [P][r][d_in/32]
+    return forward_launch(M, d_in, d_out, r, P, x, bits_u, bits_v, h, l, g, y, accumulate_y, tape_a, tape_c, bits_vt,
+                          (hipStream_t)stream);
+}
+
 int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
                 const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y, int accumulate_y,
                 float *tape_a, float *tape_c, void *workspace, size_t workspace_bytes, void *stream) {
     return forward_impl(M, d_in, d_out, r, 1, x, bits_u, bits_v, h, l, g, y, accumulate_y, tape_a, tape_c, workspace,
                         workspace_bytes, stream);
+}
+
+// ------------------------------------------------------ no allocation --
+// The allocation-free forward's scratch: room for the transposed S_V bitmap.
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code this name is not a device address: the address each device
+// uses comes from hipGetSymbolAddress (scratch_on_device below).
+static __device__ __align__(256) uint8_t scratch[BLR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+void *g_scratch_ptr[64];  // per device, looked up on its first call
+std::mutex g_scratch_mu;
+
+int scratch_on_device(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BLR_ERR_HIP;
+    if (dev < 0 || dev >= 64) return BLR_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return BLR_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BLR_OK;
+}
+}  // namespace
+
+int blr_forward_noalloc(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
+                        const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y,
+                        int accumulate_y, float *tape_a, float *tape_c, void *stream) {
+    int st = forward_check(M, d_in, d_out, r, 1, x, bits_u, bits_v, h, l, g, y, tape_a, tape_c);
+    if (st != BLR_OK) return st;
+    if ((uint64_t)r * (uint64_t)d_in / 8 > (uint64_t)BLR_NOALLOC_SCRATCH_BYTES) return BLR_ERR_SCRATCH;
+    st = current_device_ok();
+    if (st != BLR_OK) return st;
+    void *bits_vt = nullptr;
+    st = scratch_on_device(&bits_vt);
+    if (st != BLR_OK) return st;
+    return forward_launch(M, d_in, d_out, r, 1, x, bits_u, bits_v, h, l, g, y, accumulate_y, tape_a, tape_c,
+                          (uint32_t *)bits_vt, (hipStream_t)stream);
 }
 
 int blr_forward_paths(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t paths, const float *x,

@@ -58,7 +58,8 @@ typedef enum {
     BLR_ERR_WORKSPACE = -4, /* workspace NULL or smaller than blr_workspace_bytes() */
     BLR_ERR_DEVICE = -5,    /* current device is not gfx950 */
     BLR_ERR_HIP = -6,       /* the HIP runtime reported an error */
-    BLR_ERR_ALIGN = -7      /* a pointer is not 16-byte aligned */
+    BLR_ERR_ALIGN = -7,     /* a pointer is not 16-byte aligned */
+    BLR_ERR_SCRATCH = -8    /* sizes exceed the allocation-free forward's scratch */
 } blr_status;
 
 /* Human-readable text of a status code (static storage). */
@@ -104,6 +105,26 @@ int blr_expand_signs(const uint32_t *bits, int64_t rows, int64_t r, uint16_t *pl
 int blr_forward(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
                 const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y, int accumulate_y,
                 float *tape_a, float *tape_c, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Arguments, rules and results are those
+ * of blr_forward (bit for bit, the same kernels), without the workspace.
+ * The forward's only scratch, the transposed S_V bitmap (r * d_in / 8
+ * bytes), goes to a device array of BLR_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends; its address
+ * is looked up (not allocated) on the first call on each device. Nothing in
+ * it needs clearing: every call writes the part it reads. Sizes with
+ * r * d_in / 8 > BLR_NOALLOC_SCRATCH_BYTES return BLR_ERR_SCRATCH before
+ * anything is enqueued. Every call on one GPU shares that GPU's array, so
+ * calls that overlap on a GPU (other streams, other host threads) race:
+ * order them on one stream.
+ */
+#define BLR_NOALLOC_SCRATCH_BYTES (4u << 20)
+int blr_forward_noalloc(int64_t M, int64_t d_in, int64_t d_out, int64_t r, const float *x, const uint32_t *bits_u,
+                        const uint32_t *bits_v, const float *h, const float *l, const float *g, float *y,
+                        int accumulate_y, float *tape_a, float *tape_c, void *stream);
 
 /*
  * Backward (page: `blr_backward`, doc block backward lines).

@@ -14,7 +14,7 @@ import binary_rank_linear_amd as blr
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "blr.h")
 
-BLR_OK, E_NULL, E_SHAPE, E_SCALE, E_WS, E_DEV, E_HIP, E_ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+BLR_OK, E_NULL, E_SHAPE, E_SCALE, E_WS, E_DEV, E_HIP, E_ALIGN, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 def declared_functions():
@@ -47,7 +47,7 @@ def test_library_is_gfx950_only():
 
 
 def test_status_strings():
-    for s in (BLR_OK, E_NULL, E_SHAPE, E_SCALE, E_WS, E_DEV, E_HIP, E_ALIGN):
+    for s in (BLR_OK, E_NULL, E_SHAPE, E_SCALE, E_WS, E_DEV, E_HIP, E_ALIGN, E_SCRATCH):
         assert blr.status_string(s) and blr.status_string(s) != "unknown status"
     assert blr.status_string(-99) == "unknown status"
 
@@ -262,3 +262,37 @@ def test_paths_workspace_and_rejects(ptrs):
     assert lib.blr_backward_paths(128, 256, 256, 128, 2, q["x"], q["dy"], q["bu"], q["bv"], q["h"], q["l"], q["g"],
                                   q["ta"], ctypes.c_float(1024.0), q["dh"], q["dl"], q["dg"], q["dx"], 0, f(), None,
                                   0, q["ws"], ws, None) == E_NULL
+
+
+def fwd_noalloc(lib, M, d_in, d_out, r, ptrs):
+    return lib.blr_forward_noalloc(M, d_in, d_out, r, ptrs["x"], ptrs["bu"], ptrs["bv"], ptrs["h"], ptrs["l"],
+                                   ptrs["g"], ptrs["y"], 0, ptrs["ta"], ptrs["tc"], None)
+
+
+def test_forward_noalloc_rejects_before_any_device_work(ptrs):
+    """The allocation-free forward validates as blr_forward does, and rejects
+    sizes whose transposed bitmap (r * d_in / 8 bytes) exceeds its scratch
+    with its own status, before touching the device."""
+    lib = blr.load()
+    for k in ["x", "bu", "bv", "h", "l", "g", "y", "ta"]:
+        p = dict(ptrs)
+        p[k] = None
+        assert fwd_noalloc(lib, 128, 256, 256, 128, p) == E_NULL, k
+    for shape in [(0, 256, 256, 128), (128, 200, 256, 128), (128, 256, 256, 100)]:
+        assert fwd_noalloc(lib, *shape, ptrs) == E_SHAPE, shape
+    p = dict(ptrs)
+    p["x"] = ptrs["_fake"](256, offset=4)
+    assert fwd_noalloc(lib, 128, 256, 256, 128, p) == E_ALIGN
+    # r * d_in / 8 one step of d_in past the scratch (2048 * 16384 / 8 is
+    # exactly its size); sizes that pass every check are not called here,
+    # since these fake pointers must never reach a launch
+    assert 2048 * 16384 // 8 == blr.NOALLOC_SCRATCH_BYTES
+    assert fwd_noalloc(lib, 64, 16384 + 128, 256, 2048, ptrs) == E_SCRATCH
+    assert fwd_noalloc(lib, 64, 128, 256, 2048 * 128 + 128, ptrs) == E_SCRATCH
+    assert "scratch" in blr.status_string(E_SCRATCH)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define BLR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == blr.NOALLOC_SCRATCH_BYTES
