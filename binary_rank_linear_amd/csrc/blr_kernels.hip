@@ -1483,7 +1483,10 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
         case GEMM_DH:
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s);
-        case GEMM_B1: return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
+        case GEMM_B1:
+            if ((a.path_n ? a.path_n : a.N) % 256 == 0)
+                return launch_gemm_t<64, 256, 1, 4, 4, 1, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
+            return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
         case GEMM_B2:
             if (as) return launch_gemm_as<false, true, true>(K_GEMM_B2, a, s);
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, true, 8, false, 4>(K_GEMM_B2, a, s)
