@@ -234,9 +234,14 @@ __device__ __forceinline__ half8_t sign_frag_h(uint32_t w, uint32_t sel, uint32_
 }
 
 // Bitmap transpose: out [r][rows/32] from bits [rows][r/32]. A wavefront
-// takes 64 rows x one word column (32 ranks): each lane loads its row's word,
-// then one wave-wide ballot per bit position gives, for rank 32w+b, the
-// 64-bit mask of those rows; lane b keeps it and writes the two output words.
+// takes 64 rows x one word column (32 ranks): lane i loads row i's word, and
+// the two 32 x 32 bit blocks (rows 0-31 and 32-63) are transposed across the
+// lanes in five swap stages, lanes i and i ^ j exchanging the j x j
+// sub-blocks that sit off the diagonal (j = 16, 8, 4, 2, 1). Lane b then
+// holds rank 32 w + (b % 32) of its 32 rows, one output word, and lanes b
+// and b + 32 store the two adjacent words of that rank. Consecutive waves
+// take consecutive word columns of one row block, so a workgroup reads whole
+// 64-byte row segments.
 __global__ __launch_bounds__(256) void transpose_bits_kernel(const uint32_t *__restrict__ bits, int64_t rows,
                                                              int64_t r, uint32_t *__restrict__ out) {
     const int64_t W = r / 32, rw = rows / 32;
@@ -248,18 +253,20 @@ __global__ __launch_bounds__(256) void transpose_bits_kernel(const uint32_t *__r
     if (wid >= nrb * W) return;  // uniform per wavefront
     const int64_t rb = wid / W, w = wid % W;
     const int64_t row = rb * 64 + lane;
-    const uint32_t word = row < rows ? bits[row * W + w] : 0u;
-    uint64_t mine = 0;
+    uint32_t a = row < rows ? bits[row * W + w] : 0u;
+    const uint32_t masks[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
 #pragma unroll
-    for (int b = 0; b < 32; ++b) {
-        const uint64_t m = __ballot((word >> b) & 1u);
-        if (lane == b) mine = m;
+    for (int st = 0; st < 5; ++st) {
+        const int j = 16 >> st;
+        const uint32_t pv = (uint32_t)__shfl_xor((int)a, j);  // j < 32: within the lane's half
+        const bool up = (lane & j) != 0;
+        const uint32_t hi = up ? a : pv, lo = up ? pv : a;
+        const uint32_t t = ((lo >> j) ^ hi) & masks[st];
+        a ^= up ? t : (t << j);
     }
-    if (lane < 32) {
-        uint32_t *dst = out + (w * 32 + lane) * rw + rb * 2;
-        dst[0] = (uint32_t)mine;
-        if (rb * 2 + 1 < rw) dst[1] = (uint32_t)(mine >> 32);
-    }
+    // lane: rank 32 w + lane % 32, bit i = row 64 rb + 32 (lane / 32) + i
+    const int64_t ow = rb * 2 + (lane >> 5);
+    if (ow < rw) out[(w * 32 + (lane & 31)) * rw + ow] = a;
 }
 
 hipError_t launch_transpose_bits(const uint32_t *bits, int64_t rows, int64_t r, uint32_t *out, hipStream_t s,
@@ -320,7 +327,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     constexpr int LDR = BM + 16;
 
     __shared__ __attribute__((aligned(16))) _Float16 As[NS * BM * LDK];
-    __shared__ float red[DOT ? WM * BN : 1];
+    // column partials (DOT) have one row per 64 tokens: a 128-row tile
+    // (one row of waves, each with all 128 rows of its columns) writes two
+    constexpr int HR = BM / 64;
+    static_assert(BM == 64 || (BM == 128 && WM == 1 && !FDH && !MP), "128-row tiles: one row of waves");
+    __shared__ float red[DOT ? HR * WM * BN : 1];
     constexpr int NSD = 4;          // fused dh: depth of the dy ring (a step's dot runs one step late)
     __shared__ __attribute__((aligned(16))) float dyT[FDH ? NSD * 32 * LDR : 1];  // [buf][column][row]
     __shared__ float redh[FDH ? 2 * WN * 64 : 1];                                // [step & 1][wave][lane]
@@ -809,9 +820,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     float c2[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) c2[j] = (OUT2 && !MP) ? p.out2col[cb + j * 32] : 0.0f;
-    float dsum[FN];
+    float dsum[HR][FN];  // [64-row half of the wave's rows][column block]
 #pragma unroll
-    for (int j = 0; j < FN; ++j) dsum[j] = 0.0f;
+    for (int h = 0; h < HR; ++h)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dsum[h][j] = 0.0f;
     // (GUARD: check rows against M; ACC: y or dx accumulate, so the old
     // values are loaded. The common case, a full tile written without
     // accumulation, has its own copy with no load: a load under a
@@ -834,7 +847,7 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                         const float val = MP ? yacc[i][j][v] : acc[i][j][v] * osc;         \
                         if (OUT) store_f32(rO, loff, BLR_UOFF(i, v, j), val);              \
                         if (OUT2) store_f32_nt(rO2, loff, BLR_UOFF(i, v, j), old[j][v] + (MP ? val : val * c2[j])); \
-                        if (DOT && !MP) dsum[j] += val * oth[j][v];                        \
+                        if (DOT && !MP) dsum[HR == 1 ? 0 : i / 2][j] += val * oth[j][v];  \
                     }                                                                      \
                 }                                                                          \
             }                                                                              \
@@ -854,17 +867,20 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
         // column strip add in row order
         if (!dhw) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                dsum[j] += __shfl_xor(dsum[j], 32);
-                if (lane < 32) red[wm * BN + wn * TN + j * 32 + lane] = dsum[j];
-            }
+            for (int h = 0; h < HR; ++h)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const float t_ = dsum[h][j] + __shfl_xor(dsum[h][j], 32);
+                    if (lane < 32) red[(h * WM + wm) * BN + wn * TN + j * 32 + lane] = t_;
+                }
         }
         __syncthreads();
-        for (int c = tid; c < BN && tid < NT; c += NT) {
+        for (int c = tid; c < HR * BN && tid < NT; c += NT) {
+            const int h = c / BN, cc = c - h * BN;
             float sum = 0.0f;
 #pragma unroll
-            for (int w = 0; w < WM; ++w) sum += red[w * BN + c];
-            p.dot_partial[(int64_t)mt * N + n0 + c] = sum;
+            for (int w = 0; w < WM; ++w) sum += red[(h * WM + w) * BN + cc];
+            if ((int64_t)(mt * HR + h) * 64 < M) p.dot_partial[((int64_t)mt * HR + h) * N + n0 + cc] = sum;
         }
     }
 }
@@ -1464,11 +1480,19 @@ int b1dh_tile_rows(int64_t r) { return b1dh_cols(r) ? 64 : 0; }
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     const bool wide = a.N % 256 == 0;
     const bool as = wide && a.K <= AS_KMAX;  // activation block held in LDS
+    // F1 and B1 (N = r, K a model dimension) on 128 x 256 tiles (8 waves of
+    // 128 x 32, 32-wide K steps) when that still gives at least 256
+    // workgroups: each decoded sign fragment feeds four MFMAs instead of two.
+    // Measured at r = 1024 and 2048: 16-20% faster than 64 x 256 tiles; the
+    // short-K kinds (F2, DH, B2) were 5-18% slower on them, so they keep
+    // 64-row tiles
+    const bool t128 = wide && !a.path_n && !a.path_k && ((a.M + 127) / 128) * (a.N / 256) >= 256;
     switch (kind) {
         case GEMM_F1:
             // 256 columns per tile when they stay inside one path: the x tile
             // is staged once for twice the columns, and with one workgroup per
             // CU four stages of x are loaded ahead
+            if (t128) return launch_gemm_t<128, 256, 1, 8, 2, 1, true, false, false, 1, false, 2>(K_GEMM_F1, a, s);
             if ((a.path_n ? a.path_n : a.N) % 256 == 0)
                 return launch_gemm_t<64, 256, 1, 4, 4, 1, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
             return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
@@ -1484,6 +1508,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s);
         case GEMM_B1:
+            if (t128) return launch_gemm_t<128, 256, 1, 8, 2, 1, true, false, true, 1, false, 2>(K_GEMM_B1, a, s);
             if ((a.path_n ? a.path_n : a.N) % 256 == 0)
                 return launch_gemm_t<64, 256, 1, 4, 4, 1, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
             return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
