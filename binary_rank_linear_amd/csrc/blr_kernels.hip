@@ -914,6 +914,9 @@ static hipError_t launch_gemm_t(int id, const GemmArgs &a, hipStream_t s) {
 // loads and stores share one counter). The column partials need no
 // cross-wave sum: every wave holds all 64 rows of its columns.
 constexpr int AS_BM = 64, AS_BN = 256, AS_KMAX = 512;  // LDS: 64 x (K + 8) halves, 66.5 KB at K = 512
+// K = 1024 also takes the held block (129 KB of LDS: one workgroup per CU,
+// eight waves of 64 x 32 for every kind, two a SIMD)
+constexpr int AS_KBIG = 1024;
 
 // PR > 0: several paths along K, PR * 128 ranks each (K = paths * PR * 128),
 // the bitmap of path q at Bbits + q * b_pstride words ([N][PR * 4] words),
@@ -921,7 +924,7 @@ constexpr int AS_BM = 64, AS_BN = 256, AS_KMAX = 512;  // LDS: 64 x (K + 8) halv
 // (rounded to f16) is folded into its decoded signs, so one sweep over K
 // forms the sum (no column partials in this mode).
 template <int KG, int TPW, bool OUT, bool OUT2, bool DOT, int PR = 0, int NWV = 4>
-__global__ __launch_bounds__(64 * NWV, NWV / 2) void gemm_as_kernel(GemmArgs p, int groups_n) {
+__global__ __launch_bounds__(64 * NWV, KG > 4 ? 2 : NWV / 2) void gemm_as_kernel(GemmArgs p, int groups_n) {
     constexpr int K = 128 * KG, LDK = K + 8;
     static_assert(PR == 0 || (OUT2 && !OUT && !DOT && KG % PR == 0), "paths folded along K");
     constexpr int NP = PR ? KG / PR : 1;  // paths
@@ -1184,6 +1187,13 @@ static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
     if (a.N % AS_BN != 0 || a.K != 128 * KG) return hipErrorInvalidValue;
     const int64_t mtiles = (a.M + AS_BM - 1) / AS_BM;
     const int ntiles = a.N / AS_BN;
+    if constexpr (KG > 4) {
+        // one workgroup per CU: runs of four tiles while that leaves a
+        // workgroup for every CU, else two, else one
+        if (ntiles % 4 == 0 && mtiles * (ntiles / 4) >= 256) return launch_gemm_as_tt<KG, 4, OUT, OUT2, DOT, PR, 8>(id, a, s);
+        if (ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 256) return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT, PR, 8>(id, a, s);
+        return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT, PR, 8>(id, a, s);
+    } else {
     // the longest run of tiles (its words fit in registers: TPW * KG <= 16)
     // that still gives about two workgroups per CU; the runs of one M tile
     // land on one XCD. Without the dot operand every run takes 8 waves of
@@ -1197,6 +1207,7 @@ static hipError_t launch_gemm_as_t(int id, const GemmArgs &a, hipStream_t s) {
         if (ntiles % 2 == 0 && mtiles * (ntiles / 2) >= 512) return launch_gemm_as_tt<KG, 2, OUT, OUT2, DOT, PR, 8>(id, a, s);
     }
     return launch_gemm_as_tt<KG, 1, OUT, OUT2, DOT, PR, DOT ? 4 : 8>(id, a, s);
+    }
 }
 
 // B2 of a layer of NP paths on the held activation block (K = NP paths of
@@ -1461,6 +1472,7 @@ static hipError_t launch_gemm_as(int id, const GemmArgs &a, hipStream_t s) {
         case 256: return launch_gemm_as_t<2, OUT, OUT2, DOT>(id, a, s);
         case 384: return launch_gemm_as_t<3, OUT, OUT2, DOT>(id, a, s);
         case 512: return launch_gemm_as_t<4, OUT, OUT2, DOT>(id, a, s);
+        case 1024: return launch_gemm_as_t<8, OUT, OUT2, DOT>(id, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1479,7 +1491,7 @@ int b1dh_tile_rows(int64_t r) { return b1dh_cols(r) ? 64 : 0; }
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     const bool wide = a.N % 256 == 0;
-    const bool as = wide && a.K <= AS_KMAX;  // activation block held in LDS
+    const bool as = wide && (a.K <= AS_KMAX || a.K == AS_KBIG);  // activation block held in LDS
     // F1 and B1 (N = r, K a model dimension) on 128 x 256 tiles (8 waves of
     // 128 x 32, 32-wide K steps) when that still gives at least 256
     // workgroups: each decoded sign fragment feeds four MFMAs instead of two.
@@ -1505,6 +1517,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, true, false, 8, false, 4>(K_GEMM_F2, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, true, false, 8, false, 4>(K_GEMM_F2, a, s);
         case GEMM_DH:
+            if (as) return launch_gemm_as<false, false, true>(K_GEMM_DH, a, s);
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s);
         case GEMM_B1:

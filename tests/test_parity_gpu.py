@@ -71,6 +71,8 @@ SMALL = [
     (1, 128, 128, 128),     # one token
     (129, 256, 640, 384),   # one row past a tile
     (513, 1024, 256, 512),  # wide d_in, tail of 1
+    (200, 256, 512, 384),   # r = 384 with d_out a multiple of 256: the held-activation c recompute
+    (300, 512, 768, 1024),  # r = 1024: held-activation F2, c recompute and B2 on 1024 ranks, ragged tail
 ]
 
 
