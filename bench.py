@@ -47,8 +47,8 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
     per-column scales). flops: the method's own work in that launch (its
     contraction, or its column reduction). executed flops: what the launch
     performs, which differs where c is recomputed for dh (the page reads c
-    from its tape; recomputing it is this build's choice, not the method's
-    work)."""
+    from its tape; recomputing it is an implementation choice, not the
+    method's work)."""
     M, di, do, r = w.M, w.d_in, w.d_out, w.r
     f32 = 4
     if name == "gemm_f1_xg_sv":      # read x, write tape a; bitmap of S_V
@@ -406,7 +406,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer's data-parallel split and its "
-              "gradient all-reduce are not part of this build.", file=sys.stderr)
+              "gradient all-reduce are not implemented here.", file=sys.stderr)
         sys.exit(2)
 
     import torch
