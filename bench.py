@@ -18,6 +18,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -92,14 +93,23 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
     return 0.0, 0.0, 0.0
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and blank space, so that editing a
+    comment leaves the digest of the code as it was."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
-    """sha256 (first 16 hex digits) of the HIP library's sources: a profile
-    summary records the digest of the kernels it measured."""
+    """sha256 (first 16 hex digits) of the HIP library's code (comments and
+    layout left out): a profile summary records the digest of the kernels it
+    measured."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "binary_rank_linear_amd", "csrc", "*"))):
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

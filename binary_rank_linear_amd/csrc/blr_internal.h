@@ -14,8 +14,8 @@ namespace blr {
 constexpr int GEMM_BM_MIN = 64;
 // Tokens per partial of the standalone column reduction.
 constexpr int COLSUM_ROWS = 64;
-// Fewest tokens per row of the dh / dl partial buffers (B1 with dh fused
-// uses 32-row tiles).
+// Tokens per row of the dl partial buffer as sized (every producer writes
+// one row per 64 tokens, within this).
 constexpr int PART_ROWS_MIN = 32;
 
 // Kernel kinds, for per-kernel timing.

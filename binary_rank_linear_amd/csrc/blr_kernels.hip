@@ -114,24 +114,25 @@ hipError_t launch_expand(const ExpandJobs &jobs, hipStream_t s) {
 // f16 MFMA contraction with fused staging (page: `cvt_col` feeding `mm`,
 // then `scale_acc` / `colsum_prod`):
 //   prod[m][n] = (sum_k f16(A[m][k] * (colscale[k] * ascale)) * S[n][k]) * oscale
-// S is the +-1 plane [N][K], read as its bitmap (one u32 per plane row per
-// K step of 32) and decoded to f16 in registers: the page's expanded f16
+// S is the +-1 plane [N][K], read as its bitmap (a u32 holds 32 k of a
+// plane row) and decoded to f16 in registers: the page's expanded f16
 // planes are never materialised. ascale is a power of two, so folding it
 // into colscale is exact except where an f32 intermediate would overflow.
 //
 // A workgroup of WM x WN waves computes a BM x BN tile; each wave owns a
-// TM x TN block of it. Per K step of 32:
+// TM x TN block of it. Per K step (BK = 64 for the plain kinds, 32 for the
+// fused dh launch and the 128-row tiles):
 //  - activation: every thread keeps P stages of float4 loads in flight in a
-//    register ring (8 threads per row, so one wave load covers 8 whole
-//    128-byte rows). A stage is scaled and rounded to f16 with one fused
-//    multiply-and-convert per element and written to a 3-deep LDS ring two
-//    steps before it is used;
+//    register ring (16 threads per row at K steps of 64, so one wave load
+//    covers 4 whole 256-byte row segments). A stage is scaled and rounded to
+//    f16 (a multiply and a packed conversion per pair of elements) and
+//    written to a 3-deep LDS ring two steps before it is used;
 //  - each wave reads the next step's A fragments from LDS while this
 //    step's MFMAs (v_mfma_f32_32x32x16_f16, f32 accumulators) run; one
 //    barrier per step;
 //  - sign operand: each wave decodes its own B fragments from the bitmap
-//    words (fetched 4 steps at a time, one group ahead) straight into
-//    registers; it never passes through LDS;
+//    words (fetched as 16-byte groups of 128 k, one group ahead) straight
+//    into registers; it never passes through LDS;
 //  - epilogue straight from the accumulators: for a fixed accumulator
 //    register the 64 lanes hold 2 rows x 32 consecutive columns, so every
 //    store instruction writes two whole 128-byte lines.
@@ -1477,15 +1478,9 @@ static hipError_t launch_gemm_as(int id, const GemmArgs &a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-// Tile shapes per kind (measured at M=8192, d=4096, r=512): 64-row tiles of
-// 1x4 waves, two workgroups per CU so that one's prologue and epilogue
-// overlap the other's main loop, and K steps of 64 (one barrier per 4 MFMA
-// k-blocks). F1 and B1 (N = r, K = d) use 64x128 tiles
-// (64x32 per wave). F2, DH and B2 (N = d_out or d_in, K = r) use 64x256
-// tiles (64x64 per wave) when N is a multiple of 256, else 64x128, and walk
-// groups of 8 M tiles per N tile. Every kind uses 64-row tiles, so the
-// column partials have ceil(M/64) rows.
-int gemm_tile_rows(GemmKind kind) { return kind == GEMM_B1_DH ? 32 : 64; }
+// Every kind writes its column partials in rows of 64 tokens (the 128-row
+// tiles write two), so they have ceil(M/64) rows.
+int gemm_tile_rows(GemmKind) { return 64; }
 int b1dh_cols(int64_t r) { return (r == 128 || r == 256) ? (int)r : r == 512 ? 256 : 0; }
 int b1dh_tile_rows(int64_t r) { return b1dh_cols(r) ? 64 : 0; }
 
