@@ -84,8 +84,9 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
     if name == "transpose_bits":     # one bitmap in, its transpose out (average of U and V)
         return 2 * r * (di + do) / 2 / 8, 0.0, 0.0
     if name == "colsum_finish":      # read the column partials of dh, dl, dg
-        mt = -(-M // 64)  # every producer uses 64-token tiles; fused dh at r = 512: two rank tiles
-        rows_h = 2 * mt if (not keep_c and r == 512) else mt
+        mt = -(-M // 64)  # every producer uses 64-token tiles; the fused dh launch one per rank tile
+        cols = 0 if r not in (128, 256, 512) else (128 if r == 128 or mt * (r // 256) < 128 else 256)
+        rows_h = mt * (r // cols) if (not keep_c and cols) else mt
         return (rows_h * do + mt * (r + di)) * f32, 0.0, 0.0
     if name == "expand_signs":       # per launch: one bitmap in, one f16 plane out (average of U and V)
         rows = (di + do) / 2
@@ -341,6 +342,30 @@ def measure(names: list[str], label: str, dev, args, cpu_s: float) -> dict:
     return rep
 
 
+def decode_pass(L: Layer, args) -> dict:
+    """The standalone sign decode (`blr_expand_signs`, the pages' `expand`):
+    each of the layer's bitmaps into its f16 plane and transposed plane, one
+    launch per bitmap. Algorithmic bytes per launch: the bitmap read once and
+    both planes written once (rows r / 8 + 2 rows r 2)."""
+    import torch
+    blr, t, w = L.blr, L.t, L.w
+    jobs = [(t["bits_u"], w.d_out), (t["bits_v"], w.d_in)]
+    planes = [(torch.empty((rows, w.r), dtype=torch.float16, device=b.device),
+               torch.empty((w.r, rows), dtype=torch.float16, device=b.device)) for b, rows in jobs]
+
+    def run():
+        for (b, rows), (pl, plt) in zip(jobs, planes):
+            blr.blr_expand_signs(b, rows, w.r, plane=pl, plane_t=plt)
+
+    run()
+    prof = kernel_profile(blr, run, args.steps)
+    cnt, tot = prof["expand_signs"]
+    us = 1000.0 * tot / cnt
+    nbytes = sum(rows * w.r / 8 + 2 * rows * w.r * 2 for _, rows in jobs) / len(jobs)
+    return {"launches": 2, "avg_us": round(us, 3), "algorithmic_bytes": int(nbytes),
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def extras(L: Layer, dev, args) -> tuple[dict | None, dict | None]:
     """Context on the headline layer (not part of its step): the sign
     gradients of blr_backward_signs, and the layer of two paths of half the
@@ -439,9 +464,10 @@ def main():
         return list(PAIR) if label == PAIR_NAME else [label]
 
     head = measure(names_of(args.workload), args.workload, dev, args, 10.0)
-    sign = multi = None
+    sign = multi = decode = None
     if not args.no_extras and args.workload in synth.WORKLOADS:
         sign, multi = extras(head["_layers"][0], dev, args)
+        decode = decode_pass(head["_layers"][0], args)
     del head["_layers"]
     torch.cuda.empty_cache()
 
@@ -480,6 +506,7 @@ def main():
         out[k] = head[k]
     out["sign_grads"] = sign
     out["multi_path"] = multi
+    out["decode_pass"] = decode
     out["configs"] = configs
     out["cpu_baseline"] = head["cpu_baseline"]
     print(json.dumps(out), flush=True)

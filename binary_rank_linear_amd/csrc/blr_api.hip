@@ -76,12 +76,14 @@ Layout layout(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int64_t P = 1) 
     off += up((size_t)(P * r * ((d_in > d_out ? d_in : d_out) / 32)) * 4);
     L.db = off;
     off += up((size_t)(M * P * r) * 4);
-    // dh partials: 2 * ceil(M/64) rows per path (>= ceil(M/32)) cover every
-    // producer (the c-tape column sum, the recomputed-c contraction, B1 with
-    // dh fused on 64-token tiles of up to two rank halves); dl partials: one
-    // row per 32 tokens; dg partials: one row per 64 tokens and path
+    // dh partials per path: ceil(M/64) rows from the c-tape column sum or the
+    // recomputed-c contraction, ceil(M/64) per rank tile from B1 with dh
+    // fused (up to four tiles of 128 ranks); dl partials: one row per 32
+    // tokens; dg partials: one row per 64 tokens and path
+    const int64_t bc = b1dh_cols(M, r, P);
+    const int64_t hrows = ceil_div(M, GEMM_BM_MIN) * (bc ? r / bc : 1);
     L.part_h = off;
-    off += up((size_t)(2 * P * ceil_div(M, GEMM_BM_MIN) * d_out) * 4);
+    off += up((size_t)(P * hrows * d_out) * 4);
     L.part_l = off;
     off += up((size_t)(ceil_div(M, PART_ROWS_MIN) * P * r) * 4);
     L.part_g = off;
@@ -375,7 +377,8 @@ static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int6
     float *part_g = (float *)(ws + L.part_g);
     const float inv = 1.0f / gscale;  // exact: gscale is a power of two
     const int64_t Pr = P * r;
-    const bool fused = tape_c == nullptr && b1dh_cols(r) > 0;  // B1 with dh fused
+    const int64_t b1dh_c = b1dh_cols(M, r, P);
+    const bool fused = tape_c == nullptr && b1dh_c > 0;  // B1 with dh fused
     const int64_t mt_b1 = ceil_div(M, fused ? b1dh_tile_rows(r) : gemm_tile_rows(GEMM_B1));
     const int64_t mt_b2 = ceil_div(M, gemm_tile_rows(P > 1 ? GEMM_B2_MP : GEMM_B2));
 
@@ -386,7 +389,7 @@ static int backward_impl(int64_t M, int64_t d_in, int64_t d_out, int64_t r, int6
     // (same tiles, so the same c)
     int64_t nparts_h = 0;
     if (fused) {
-        nparts_h = mt_b1 * (r / b1dh_cols(r));  // one row per (rank tile, row tile) of the path
+        nparts_h = mt_b1 * (r / b1dh_c);  // one row per (rank tile, row tile) of the path
     } else if (tape_c) {
         BLR_TRY(launch_colsum(dy, tape_c, M, (int)d_out, part_h, s));
         nparts_h = ceil_div(M, COLSUM_ROWS);

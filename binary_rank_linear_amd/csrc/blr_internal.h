@@ -90,11 +90,15 @@ enum GemmKind {
 };
 // Most paths of one layer the fused launches serve.
 constexpr int MAX_PATHS = 4;
-// GEMM_B1_DH tiles: rank columns and token rows per workgroup (0 where the
-// fused launch does not serve r). The dh partials have
-// ceil(M / b1dh_tile_rows(r)) * (r / b1dh_cols(r)) rows, at most
-// 2 * ceil(M / 64); the dl partials ceil(M / b1dh_tile_rows(r)).
-int b1dh_cols(int64_t r);
+// Fewer 64 x 256 tiles than this leave most CUs idle: F1, B1 and the fused
+// B1_DH then take 128-column tiles.
+constexpr int64_t SMALL_GRID = 128;
+// GEMM_B1_DH tiles for M tokens and P paths of r ranks: rank columns and
+// token rows per workgroup (0 where the fused launch does not serve r). The
+// dh partials of a path have ceil(M / b1dh_tile_rows(r)) * (r /
+// b1dh_cols(M, r, P)) rows, at most 4 * ceil(M / 64); the dl partials
+// ceil(M / b1dh_tile_rows(r)).
+int b1dh_cols(int64_t M, int64_t r, int64_t P);
 int b1dh_tile_rows(int64_t r);
 
 // Sign-plane expansion jobs (one bitmap each; pl and/or plt may be null).
