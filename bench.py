@@ -88,9 +88,9 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
         cols = 0 if r not in (128, 256, 512) else (128 if r == 128 or mt * (r // 256) < 128 else 256)
         rows_h = mt * (r // cols) if (not keep_c and cols) else mt
         return (rows_h * do + mt * (r + di)) * f32, 0.0, 0.0
-    if name == "expand_signs":       # per launch: one bitmap in, one f16 plane out (average of U and V)
-        rows = (di + do) / 2
-        return rows * (r / 8 + r * 2), 0.0, 0.0
+    if name == "expand_signs":       # per launch: one bitmap in, its f16 plane and transposed plane out
+        rows = (di + do) / 2         # (average of U and V)
+        return rows * (r / 8 + 2 * r * 2), 0.0, 0.0
     return 0.0, 0.0, 0.0
 
 
@@ -361,7 +361,7 @@ def decode_pass(L: Layer, args) -> dict:
     prof = kernel_profile(blr, run, args.steps)
     cnt, tot = prof["expand_signs"]
     us = 1000.0 * tot / cnt
-    nbytes = sum(rows * w.r / 8 + 2 * rows * w.r * 2 for _, rows in jobs) / len(jobs)
+    nbytes = kernel_work("expand_signs", w)[0]
     return {"launches": 2, "avg_us": round(us, 3), "algorithmic_bytes": int(nbytes),
             "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
