@@ -274,8 +274,12 @@ def cpu_baseline(layers: list, target_s: float) -> dict:
     M = layers[0].w.M
     n = min(M, 64)
     dt = run(n)
-    if dt < 0.4 * target_s and n < M:
-        n = int(min(M, max(n, n * target_s / max(dt, 1e-3))))
+    # a small run's time is mostly the oracle's fixed per-call work (the
+    # sign decode), so scale the sample up in a few rounds
+    for _ in range(3):
+        if dt >= 0.4 * target_s or n >= M:
+            break
+        n = int(min(M, max(n + 64, n * target_s / max(dt, 1e-3))))
         n = max(64, (n // 64) * 64) if n < M else M
         dt = run(n)
     reps = 1
