@@ -1717,7 +1717,7 @@ __global__ __launch_bounds__(512, 2) void gemm_tn_kernel(TnJobs jobs) {
 // step of 32 tokens each thread stages a 4-token x 4-column block of both
 // operands (rounded to f16, transposed into LDS), two register stages ahead.
 constexpr int TN2_T = 256, TN2_LDK = 32, TN2_TP = 2;
-__global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int splits, int64_t tps, int64_t part_stride) {
+__global__ __launch_bounds__(512, 1) void gemm_tn2_kernel(TnJobs jobs, int64_t tps, int64_t part_stride) {
     __shared__ __attribute__((aligned(16))) _Float16 As[2][TN2_T * TN2_LDK];
     __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TN2_T * TN2_LDK];
     const int G = gridDim.x;
@@ -1911,7 +1911,7 @@ hipError_t launch_gemm_tn(TnJobs jobs, hipStream_t s) {
             total += (jobs.job[j].Mo / TN2_T) * (jobs.job[j].No / TN2_T) * splits;
         }
         prof_begin(K_GEMM_SIGNS, s);
-        hipLaunchKernelGGL(gemm_tn2_kernel, dim3((unsigned)total), dim3(512), 0, s, jobs, splits, tps, elems);
+        hipLaunchKernelGGL(gemm_tn2_kernel, dim3((unsigned)total), dim3(512), 0, s, jobs, tps, elems);
         hipError_t e = hipGetLastError();
         prof_end(s);
         if (e != hipSuccess || splits == 1) return e;
