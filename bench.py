@@ -85,7 +85,7 @@ def kernel_work(name: str, w: synth.Workload, keep_c: bool = False) -> tuple[flo
         return 2 * r * (di + do) / 2 / 8, 0.0, 0.0
     if name == "colsum_finish":      # read the column partials of dh, dl, dg
         mt = -(-M // 64)  # every producer uses 64-token tiles; the fused dh launch one per rank tile
-        cols = 0 if r not in (128, 256, 512) else (128 if r == 128 or mt * (r // 256) < 128 else 256)
+        cols = 0 if r not in (128, 256, 512) else (128 if r == 128 or mt * (r // 256) <= 128 else 256)
         rows_h = mt * (r // cols) if (not keep_c and cols) else mt
         return (rows_h * do + mt * (r + di)) * f32, 0.0, 0.0
     if name == "expand_signs":       # per launch: one bitmap in, its f16 plane and transposed plane out

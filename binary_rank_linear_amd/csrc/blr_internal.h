@@ -90,8 +90,8 @@ enum GemmKind {
 };
 // Most paths of one layer the fused launches serve.
 constexpr int MAX_PATHS = 4;
-// Fewer 64 x 256 tiles than this leave most CUs idle: F1, B1 and the fused
-// B1_DH then take 128-column tiles.
+// At most this many 64 x 256 tiles (half the CUs) leave the chip half idle
+// or worse: F1, B1 and the fused B1_DH then take 128-column tiles.
 constexpr int64_t SMALL_GRID = 128;
 // GEMM_B1_DH tiles for M tokens and P paths of r ranks: rank columns and
 // token rows per workgroup (0 where the fused launch does not serve r). The

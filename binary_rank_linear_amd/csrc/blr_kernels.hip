@@ -1483,8 +1483,8 @@ static hipError_t launch_gemm_as(int id, const GemmArgs &a, hipStream_t s) {
 int gemm_tile_rows(GemmKind) { return 64; }
 int b1dh_cols(int64_t M, int64_t r, int64_t P) {
     if (r != 128 && r != 256 && r != 512) return 0;
-    // 256 ranks a workgroup, or 128 where that would leave most CUs idle
-    if (r == 128 || ((M + 63) / 64) * (P * r / 256) < SMALL_GRID) return 128;
+    // 256 ranks a workgroup, or 128 where that would leave half the CUs idle
+    if (r == 128 || ((M + 63) / 64) * (P * r / 256) <= SMALL_GRID) return 128;
     return 256;
 }
 int b1dh_tile_rows(int64_t r) { return (r == 128 || r == 256 || r == 512) ? 64 : 0; }
@@ -1500,8 +1500,8 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
     // 64-row tiles
     const bool t128 = wide && !a.path_n && !a.path_k && ((a.M + 127) / 128) * (a.N / 256) >= 256;
     // F1 and B1 on 64 x 128 tiles (two workgroups a CU) where 64 x 256 tiles
-    // would leave most CUs idle: measured at 2048 tokens, 16-18% faster
-    const bool few = ((a.M + 63) / 64) * (a.N / 256) < SMALL_GRID;
+    // would leave half the CUs idle: measured at 2048 tokens, 16-18% faster
+    const bool few = ((a.M + 63) / 64) * (a.N / 256) <= SMALL_GRID;
     switch (kind) {
         case GEMM_F1:
             // 256 columns per tile when they stay inside one path: the x tile

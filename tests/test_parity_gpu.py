@@ -365,3 +365,25 @@ def test_mid_size_full_oracle(dev, M):
     torch.cuda.synchronize()
     got = {"y": host(y), "a": host(ta), "dh": host(dh), "dl": host(dl), "dg": host(dg), "dx": host(dx)}
     assert_close(got, run_oracle(d))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [8192, 12288])
+def test_rank_256_tile_widths(dev, M):
+    """d = 4096, r = 256 on both sides of the tile-width switch: 8192 tokens
+    give 128 row tiles of 256 ranks, half the CUs, so F1, B1 and the fused
+    B1_DH take 128-column tiles; 12288 tokens give 192 and keep the 256-column
+    ones. Every token and every output against the oracle, with dense dy."""
+    import torch
+    d_in = d_out = 4096
+    r = 256
+    check_shapes_fit(M, d_in, d_out, r)
+    d = synth.custom(M, d_in, d_out, r, seed=9300 + M, dy_sigma=1e-6)
+    t = to_dev(d, dev)
+    say(f"r=256 tile widths M={M}: forward and backward")
+    y, ta, tc = blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"])
+    dh, dl, dg, dx = blr.blr_backward(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
+                                      float(d["gscale"]))
+    torch.cuda.synchronize()
+    got = {"y": host(y), "a": host(ta), "dh": host(dh), "dl": host(dl), "dg": host(dg), "dx": host(dx)}
+    assert_close(got, run_oracle(d))
