@@ -1506,10 +1506,13 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
         case GEMM_F1:
             // 256 columns per tile when they stay inside one path: the x tile
             // is staged once for twice the columns, and with one workgroup per
-            // CU four stages of x are loaded ahead
+            // CU four stages of x are loaded ahead. Eight waves of 64 x 32, two
+            // a SIMD, so one wave's decode and staging issue beside the other's
+            // MFMAs: measured 5-6% faster than four waves of 64 x 64 at 6144 to
+            // 12288 tokens (d_in = 4096, r = 512)
             if (t128) return launch_gemm_t<128, 256, 1, 8, 2, 1, true, false, false, 1, false, 2>(K_GEMM_F1, a, s);
             if ((a.path_n ? a.path_n : a.N) % 256 == 0 && !few)
-                return launch_gemm_t<64, 256, 1, 4, 4, 1, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
+                return launch_gemm_t<64, 256, 1, 8, 4, 1, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
             return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, false, 1, false, 4>(K_GEMM_F1, a, s);
         case GEMM_F2:
             if (as) return launch_gemm_as<true, true, false>(K_GEMM_F2, a, s);
@@ -1524,9 +1527,10 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs &a, hipStream_t s) {
             return wide ? launch_gemm_t<64, 256, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s)
                         : launch_gemm_t<64, 128, 1, 4, 2, 2, false, false, true, 8, false, 4>(K_GEMM_DH, a, s);
         case GEMM_B1:
+            // (the same tiles as F1; eight waves measured 6% faster here too)
             if (t128) return launch_gemm_t<128, 256, 1, 8, 2, 1, true, false, true, 1, false, 2>(K_GEMM_B1, a, s);
             if ((a.path_n ? a.path_n : a.N) % 256 == 0 && !few)
-                return launch_gemm_t<64, 256, 1, 4, 4, 1, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
+                return launch_gemm_t<64, 256, 1, 8, 4, 1, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
             return launch_gemm_t<64, 128, 1, 4, 2, 2, true, false, true, 1, false, 4>(K_GEMM_B1, a, s);
         case GEMM_B2:
             if (as) return launch_gemm_as<false, true, true>(K_GEMM_B2, a, s);
