@@ -368,6 +368,29 @@ def test_mid_size_full_oracle(dev, M):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("keep_c", [False, True])
+def test_eight_wave_tiles_ragged_rows(dev, keep_c):
+    """d = 4096, r = 512 at 6100 tokens: 96 row tiles of 256 ranks, so F1
+    (and, with the c tape, the plain B1) take the 64 x 256 tiles of eight
+    64 x 32 waves, the last row tile holding 20 tokens. Every token and every
+    output against the oracle, with dense dy."""
+    import torch
+    M, d_in, d_out, r = 6100, 4096, 4096, 512
+    check_shapes_fit(M, d_in, d_out, r)
+    d = synth.custom(M, d_in, d_out, r, seed=9500 + int(keep_c), dy_sigma=1e-6)
+    t = to_dev(d, dev)
+    say(f"eight-wave tiles M={M} keep_c={keep_c}: forward and backward")
+    y, ta, tc = blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], keep_c=keep_c)
+    dh, dl, dg, dx = blr.blr_backward(t["x"], t["dy"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
+                                      float(d["gscale"]))
+    torch.cuda.synchronize()
+    got = {"y": host(y), "a": host(ta), "dh": host(dh), "dl": host(dl), "dg": host(dg), "dx": host(dx)}
+    if keep_c:
+        got["c"] = host(tc)
+    assert_close(got, run_oracle(d))
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("M", [8192, 12288])
 def test_rank_256_tile_widths(dev, M):
     """d = 4096, r = 256 on both sides of the tile-width switch: 8192 tokens
