@@ -336,6 +336,11 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
     constexpr int NSD = 4;          // fused dh: depth of the dy ring (a step's dot runs one step late)
     __shared__ __attribute__((aligned(16))) float dyT[FDH ? NSD * 32 * LDR : 1];  // [buf][column][row]
     __shared__ float redh[FDH ? 2 * WN * 64 : 1];                                // [step & 1][wave][lane]
+    // fused dh: the tile's f32 a block, as the DH waves load it, for the B1
+    // waves' epilogue (the dl partials); the pad of 8 keeps both sides'
+    // accesses free of bank conflicts
+    constexpr int LDA_ = BN + 8;
+    __shared__ __attribute__((aligned(16))) float aL[FDH ? BM * LDA_ : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -446,6 +451,12 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
                     h[4 + e] = inr ? (_Float16)(x1[e] * l1[e]) : (_Float16)0.0f;
                 }
                 al[i * KD + t] = h;
+                if (FDH) {
+                    float *d_ = aL + (32 * i + (lane & 31)) * LDA_ + (k - n0);
+                    const f32x4_t z_ = {0.0f, 0.0f, 0.0f, 0.0f};
+                    *reinterpret_cast<f32x4_t *>(d_) = inr ? x0 : z_;
+                    *reinterpret_cast<f32x4_t *>(d_ + 4) = inr ? x1 : z_;
+                }
             }
         }
         hoff = (uint32_t)(((lane & 31) * DRW + (n0 - pn * p.path_n + wn * TN) / 32) * 4);
@@ -838,7 +849,9 @@ __global__ __launch_bounds__((FDH ? 2 : 1) * WM * WN * 64, MINB) void gemm_kerne
             _Pragma("unroll") for (int v = 0; v < 16; ++v) {                               \
                 const bool in_ = !(GUARD) || rl + i * 32 + 8 * (v >> 2) + (v & 3) < M;     \
                 _Pragma("unroll") for (int j = 0; j < FN; ++j) {                           \
-                    if (DOT && !MP) oth[j][v] = in_ ? load_f32_nt(rD, loff, BLR_UOFF(i, v, j)) : 0.0f; \
+                    if (DOT && !MP) oth[j][v] = !in_ ? 0.0f : FDH ?                                   \
+                        aL[(4 * (lane >> 5) + i * 32 + 8 * (v >> 2) + (v & 3)) * LDA_ + wn * TN + (lane & 31) + j * 32] : \
+                        load_f32_nt(rD, loff, BLR_UOFF(i, v, j));                                 \
                     if (OUT2) old[j][v] = ((ACC) && in_) ? load_f32(rO2, loff, BLR_UOFF(i, v, j)) : 0.0f; \
                 }                                                                          \
             }                                                                              \
