@@ -73,6 +73,8 @@ SMALL = [
     (513, 1024, 256, 512),  # wide d_in, tail of 1
     (200, 256, 512, 384),   # r = 384 with d_out a multiple of 256: the held-activation c recompute
     (300, 512, 768, 1024),  # r = 1024: held-activation F2, c recompute and B2 on 1024 ranks, ragged tail
+    (3000, 1024, 1280, 768),  # r = 768: F1 and B1 on 64 x 256 tiles of eight waves (three column tiles),
+                              # the generic F2, c recompute and B2; 56-row tail
 ]
 
 
