@@ -128,6 +128,20 @@ def test_rejects_bad_shapes(ptrs, shape):
     assert bwd(lib, *shape, ptrs, ws_bytes=1 << 40) == E_SHAPE
 
 
+@pytest.mark.parametrize("M,d_in,d_out,r", [(65535, 16384, 128, 128), (65535, 128, 16384, 128),
+                                           (32767, 128, 128, 32768)], ids=["x_dx", "y_dy", "db"])
+def test_operand_size_edge(ptrs, M, d_in, d_out, r):
+    """The kernels address every operand with 32-bit byte offsets: a shape
+    whose largest operand (x and dx, y and dy, or the db workspace) is one
+    token short of 4 GiB is accepted; one more token, exactly 4 GiB, is
+    rejected before any device work."""
+    lib = blr.load()
+    assert blr.blr_workspace_bytes(M, d_in, d_out, r) > 0
+    assert blr.blr_workspace_bytes(M + 1, d_in, d_out, r) == 0
+    assert fwd(lib, M + 1, d_in, d_out, r, ptrs, ws_bytes=1 << 40) == E_SHAPE
+    assert bwd(lib, M + 1, d_in, d_out, r, ptrs, ws_bytes=1 << 40) == E_SHAPE
+
+
 @pytest.mark.parametrize("gs", [0.0, -1024.0, 3.0, 1000.0, float("inf"), float("nan"), 1.5])
 def test_backward_rejects_bad_gscale(ptrs, gs):
     assert bwd(blr.load(), 128, 256, 256, 128, ptrs, gscale=gs) == E_SCALE

@@ -347,6 +347,41 @@ def test_ragged_full_size_sampled_and_properties(dev):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("M,d_in,d_out,r", [(65535, 16384, 128, 128), (65535, 128, 16384, 128)],
+                         ids=["x_dx_edge", "y_dy_edge"])
+def test_operands_at_the_size_edge(dev, M, d_in, d_out, r):
+    """x and dx (or y and dy) one token short of 4 GiB, the largest operand
+    the kernels' 32-bit byte offsets allow. With dy zero outside 48 sampled
+    tokens (the first, the last, the last of a full tile and 45 more), the
+    sampled rows of y, a and dx and all of dh, dl and dg against the oracle
+    on the sample, and dx exactly zero where dy is zero."""
+    import torch
+    check_shapes_fit(M, d_in, d_out, r)
+    d = synth.custom(M, d_in, d_out, r, seed=9700 + d_in, dy_sigma=1e-6)
+    S = sample_tokens(M)
+    t = to_dev(d, dev)
+    ws = blr.workspace(M, d_in, d_out, r, dev)
+    say(f"size edge M={M} d_in={d_in} d_out={d_out} r={r}: forward")
+    y, ta, tc = blr.blr_forward(t["x"], t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ws=ws)
+    dy_s = torch.zeros_like(t["dy"])
+    idx = torch.from_numpy(S).to(dev)
+    dy_s[idx] = t["dy"][idx]
+    del t["dy"]
+    say(f"size edge M={M}: backward with sampled dy")
+    dh, dl, dg, dx = blr.blr_backward(t["x"], dy_s, t["bits_u"], t["bits_v"], t["h"], t["l"], t["g"], ta, tc,
+                                      float(d["gscale"]), ws=ws)
+    torch.cuda.synchronize()
+    sub = {k: d[k] for k in ("bits_u", "bits_v", "h", "l", "g")}
+    sub["x"], sub["dy"] = d["x"][S], d["dy"][S]
+    got = {"y": host(y[idx]), "a": host(ta[idx]), "dh": host(dh), "dl": host(dl), "dg": host(dg),
+           "dx": host(dx[idx])}
+    assert_close(got, run_oracle(sub))
+    mask = torch.ones(M, dtype=torch.bool, device=dev)
+    mask[idx] = False
+    assert int(torch.count_nonzero(dx[mask])) == 0, "dx must be exactly zero where dy is zero"
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("M", [2048, 4000, 4096])
 def test_mid_size_full_oracle(dev, M):
     """d = 4096, r = 512 at fewer tokens than the benchmark: the held-activation
