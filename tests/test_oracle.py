@@ -448,7 +448,7 @@ def test_sumsq_closed_forms_and_non_finite():
 # ------------------------------------------------ the acceptance measure --
 # rel = ||got - want||_F / max(||want||_F, 1e-15), the measure of test
 # `blr_layer_matches_host` on the page (its `rel` closure). Every GPU parity
-# verdict rests on it, so it is pinned by values that a dropped square root,
+# check rests on it, so it is pinned by values that a dropped square root,
 # a dropped floor or a swapped argument would change.
 
 def test_rel_frobenius_closed_forms():
