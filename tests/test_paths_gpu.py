@@ -26,6 +26,8 @@ SHAPES = [
     (130, 512, 768, 128, 3),   # the same with 128 ranks a path, three paths
     (150, 512, 256, 384, 2),   # B2 on the held activation with 384 ranks a path
     (100, 256, 256, 256, 4),   # four paths of 256 ranks: a 1024-rank block in one workgroup
+    (6100, 4096, 4096, 256, 2),  # F1 on 64 x 256 tiles of eight waves inside each path, the fused dh launch on
+                                 # 256-rank tiles (one per path), a 20-row tail: every token against the oracle
 ]
 
 
