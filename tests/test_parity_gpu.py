@@ -131,6 +131,7 @@ def test_windows_workload_full_oracle(dev):
     (200, 256, 384, 128, False),   # d_out not a multiple of 256: the generic F2 and B2
     (200, 512, 512, 256, False),   # the held-activation F2 and B2 epilogues
     (130, 256, 768, 512, True),    # held activation with the c tape, ragged tail
+    (130, 512, 768, 1024, False),  # the held activation at K = 1024 (F2, the c recompute and B2 on 1024 ranks)
 ])
 def test_accumulate_flags(dev, M, d_in, d_out, r, keep_c):
     """y += h.c and dx += g.dx' when asked; dh, dl, dg always accumulate."""
