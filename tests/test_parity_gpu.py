@@ -75,6 +75,8 @@ SMALL = [
     (300, 512, 768, 1024),  # r = 1024: held-activation F2, c recompute and B2 on 1024 ranks, ragged tail
     (3000, 1024, 1280, 768),  # r = 768: F1 and B1 on 64 x 256 tiles of eight waves (three column tiles),
                               # the generic F2, c recompute and B2; 56-row tail
+    (200, 256, 384, 4096),    # large ranks: the generic F2, c recompute and B2 over K = 4096 (128 words a row)
+    (64, 128, 256, 8192),     # one row tile, K = r = 8192 (256 words a row)
 ]
 
 
