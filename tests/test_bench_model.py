@@ -77,3 +77,16 @@ def test_measured_traffic_follows_the_source_digest(tmp_path, monkeypatch):
     assert bench.measured_traffic("wl", "gemm_x") == 1234
     src.write_text("__global__ void k(float *p) { p[0] = 2.0f; }\n")
     assert bench.measured_traffic("wl", "gemm_x") is None
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_more_than_one_gpu_is_refused(n):
+    """The benchmark runs on one GPU; asked for more it says so and exits
+    with status 2 before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", str(n)], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
